@@ -1,0 +1,79 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case patches one plausible error into the oracle and checks that the
+independent reference it is pinned to disagrees.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as orc
+
+
+def _case(rng, H=3, L=50, sq=1):
+    qn = rng.standard_normal((sq, H, 128))
+    qp = rng.standard_normal((sq, H, 64))
+    wk = rng.standard_normal((H, 128, 512)) / math.sqrt(512)
+    wv = rng.standard_normal((H, 128, 512)) / math.sqrt(512)
+    c = rng.standard_normal((L, 512))
+    kr = rng.standard_normal((L, 64))
+    return qn, qp, wk, wv, c, kr
+
+
+def _brute_tiny_mismatch(monkeypatch, patch):
+    rng = np.random.default_rng(1)
+    H, dn, dr, dc, dv, L = 2, 3, 2, 5, 4, 6
+    args = (rng.standard_normal((2, H, dn)), rng.standard_normal((2, H, dr)),
+            rng.standard_normal((H, dn, dc)), rng.standard_normal((H, dv, dc)),
+            rng.standard_normal((L, dc)), rng.standard_normal((L, dr)))
+    want = orc.brute_force_decode(*args, 1 / math.sqrt(dn + dr))
+    with monkeypatch.context() as m:
+        patch(m)
+        got = orc.naive_decode(*args, 1 / math.sqrt(dn + dr))
+    return np.max(np.abs(got - want))
+
+
+def test_dropped_rope_term_is_caught(monkeypatch):
+    def patch(m):
+        m.setattr(orc, "naive_scores",
+                  lambda qn, qp, wk, c, kr, s: s * ((c @ wk.T) @ qn))
+    assert _brute_tiny_mismatch(monkeypatch, patch) > 1e-3
+
+
+def test_wrong_rope_sign_is_caught(monkeypatch):
+    def patch(m):
+        m.setattr(orc, "naive_scores",
+                  lambda qn, qp, wk, c, kr, s: s * ((c @ wk.T) @ qn - kr @ qp))
+    assert _brute_tiny_mismatch(monkeypatch, patch) > 1e-3
+
+
+def test_off_by_one_visibility_is_caught(monkeypatch):
+    def patch(m):
+        m.setattr(orc, "visible_len", lambda L, sq, i: L - sq + i)
+    assert _brute_tiny_mismatch(monkeypatch, patch) > 1e-3
+
+
+def test_wrong_scale_is_caught_by_score_std():
+    rng = np.random.default_rng(61)
+    qn, qp, wk, wv, c, kr = _case(rng, H=64, L=512)
+    for bad in (1 / 192, 1 / math.sqrt(128)):
+        s = np.concatenate([orc.naive_scores(qn[0, h], qp[0, h], wk[h], c, kr, bad)
+                            for h in range(64)])
+        assert abs(s.std() - 1) >= 0.03
+
+
+def test_unshifted_merge_weights_are_caught():
+    rng = np.random.default_rng(3)
+    qn, qp, wk, wv, c, kr = _case(rng, H=1, L=300)
+    qn *= 3
+    s = orc.default_scale()
+    _, o_lat = orc.absorb_decode(qn, qp, wk, wv, c, kr, s, return_latent=True)
+    q_abs = orc.absorb_query(qn, wk)
+    parts = [orc.absorb_partial(q_abs[0, 0], qp[0, 0], c, kr, s, t0, t0 + 100, 300)
+             for t0 in (0, 100, 200)]
+    # a merge that forgets the exp(m_s - M) rescale disagrees with one pass
+    bad = sum(o for o, _, _ in parts) / sum(l for _, _, l in parts)
+    assert np.max(np.abs(bad - o_lat[0, 0])) > 1e-3
+    assert np.max(np.abs(orc.merge_partials(parts) - o_lat[0, 0])) < 1e-12
