@@ -1,0 +1,149 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention
+ * decode library, absorbed path.
+ *
+ * What it computes. DeepSeek-V3's MLA caches, per layer and per token, only a
+ * 512-d joint KV latent c_KV and a 64-d decoupled RoPE key k_R that all heads
+ * share ("DeepSeek-V3" page at ailearn.mscapital.top, MLA section and its
+ * configuration table; m.lsln.cn article, sections 2.2 and 2.3). For a decode
+ * step the library computes, for every sequence b, new-token row i and head h:
+ *
+ *   q_abs = W_UK[h]^T q_nope[b,i,h]                          (128 -> 512)
+ *   s_j   = scale * (q_abs . c_KV,j + q_pe[b,i,h] . k_R,j)    j visible to (b,i)
+ *   p     = softmax_j(s)
+ *   o_lat = sum_j p_j c_KV,j                                   (512)
+ *   out[b,i,h] = W_UV[h] o_lat                                 (512 -> 128)
+ *
+ * i.e. the absorb order of the identity q^T (U c) = (U^T q)^T c given in the
+ * algebra check of section 2 of the wq-win.github.io DeepSeek-V3 notes: the
+ * per-head keys and values are never materialised. It equals, up to rounding,
+ * softmax attention with K_h = [W_UK[h] c ; k_R] and V_h = W_UV[h] c.
+ *
+ * Visibility: seq_lens[b] = L_b counts every cached token of sequence b,
+ * including its q_tokens new ones; new-token row i (0-based) sees positions
+ * j <= L_b - q_tokens + i (itself and everything before it). A row that sees
+ * no position (L_b < q_tokens) yields zeros.
+ *
+ * Fixed dimensions (checked at init): 128 heads, d_nope 128, d_rope 64,
+ * d_latent 512, d_v 128, cache block 64 tokens, q_tokens 1 or 2.
+ *
+ * Data layouts (all row-major, all device memory, all borrowed):
+ *   q_nope   bf16  [B, Sq, 128 heads, 128]
+ *   q_pe     bf16  [B, Sq, 128 heads, 64]       already rotated
+ *   w_uk     bf16  [128 heads, 128 (nope), 512 (latent)]   k_nope = W_UK[h] c
+ *   w_uv     bf16  [128 heads, 128 (v), 512 (latent)]      v      = W_UV[h] c
+ *   kv_cache bf16  [num_blocks, 64, 576]  each row = c_KV (512) | k_R (64),
+ *                  k_R already rotated; logical token j of sequence b lives in
+ *                  block block_table[b, j / 64], slot j % 64
+ *   block_table int32 [B, max_blocks_per_seq]; entries past ceil(L_b/64) unread
+ *   seq_lens    int32 [B]   (device memory; read only by the kernels)
+ *   out         fp32  [B, Sq, 128 heads, 128]
+ * Slots of a block past L_b may hold anything (NaN included): they are never
+ * used. Every pointer must be 16-byte aligned.
+ *
+ * Numerics: bf16 inputs are consumed exactly. The absorbed query and the
+ * softmax probabilities are rounded to fp16 and the latent tile is converted
+ * bf16 -> fp16 for the matrix-core products (exact for |c_KV| in fp16's range,
+ * i.e. |c_KV| <= 65504; larger magnitudes saturate). q_pe . k_R runs in bf16.
+ * Accumulation, the softmax and the split merge are fp32; out is fp32.
+ *
+ * Errors: every call returns an int status (MLA_OK = 0 or a negative code);
+ * no C++ exception crosses the ABI. Faults inside kernels surface at the
+ * caller's next synchronisation of the stream.
+ *
+ * Threading: a context is immutable after init; mla_decode_run may be called
+ * concurrently on different streams as long as each call has its own
+ * workspace.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mla_decode_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,     /* null pointer, non-positive size, Sq not 1/2 */
+  MLA_ERR_UNSUPPORTED = -2,     /* dims other than the compiled set, not gfx950 */
+  MLA_ERR_MISALIGNED = -3,      /* a pointer not 16-byte aligned */
+  MLA_ERR_WORKSPACE = -4,       /* workspace null or smaller than required */
+  MLA_ERR_HIP = -5,             /* a HIP runtime call or launch failed */
+};
+
+typedef struct mla_decode_config {
+  int32_t num_heads;     /* 128 */
+  int32_t d_nope;        /* 128 */
+  int32_t d_rope;        /* 64 */
+  int32_t d_latent;      /* 512 */
+  int32_t d_v;           /* 128 */
+  int32_t block_size;    /* 64 */
+  int32_t max_q_tokens;  /* 1 or 2 */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(d_nope + d_rope) */
+  int32_t split_target;  /* about how many splits to cut a batch into; 0 = one
+                            per compute unit (Sq = 1) or per two (Sq = 2) */
+} mla_decode_config;
+
+typedef struct mla_decode_args {
+  const void* q_nope;         /* bf16 [B, Sq, H, 128] */
+  const void* q_pe;           /* bf16 [B, Sq, H, 64] */
+  const void* w_uk;           /* bf16 [H, 128, 512] */
+  const void* w_uv;           /* bf16 [H, 128, 512] */
+  const void* kv_cache;       /* bf16 [num_blocks, 64, 576] */
+  const int32_t* block_table; /* int32 [B, max_blocks_per_seq] */
+  const int32_t* seq_lens;    /* int32 [B] */
+  float* out;                 /* fp32 [B, Sq, H, 128] */
+  int64_t num_blocks;         /* blocks in kv_cache */
+  int32_t batch;              /* B >= 1 */
+  int32_t q_tokens;           /* Sq: 1 or 2, <= max_q_tokens */
+  int32_t max_blocks_per_seq; /* row stride of block_table */
+  int32_t max_seq_len;        /* host upper bound on every L_b;
+                                 <= 64 * max_blocks_per_seq */
+} mla_decode_args;
+
+typedef struct mla_decode_ctx mla_decode_ctx;
+
+/* Validate cfg against the compiled dimensions, check that `hip_device` is a
+ * gfx950 GPU, and read its compute-unit count. Host only: no device memory is
+ * allocated and nothing is launched. On success *out owns a small host object
+ * released by mla_decode_destroy. */
+int mla_decode_init(const mla_decode_config* cfg, int hip_device, mla_decode_ctx** out);
+
+/* Bytes of device workspace mla_decode_run needs for a call with this batch,
+ * q_tokens and max_seq_len. Pure host arithmetic. */
+int mla_decode_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                              int32_t max_seq_len, size_t* bytes);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream):
+ * the split plan, the absorb product, the fused score / softmax / latent
+ * accumulation over the paged cache, and the split merge with the W_UV
+ * product. Never allocates, never synchronises. `workspace` is caller-owned
+ * device memory of at least mla_decode_workspace_size bytes, 256-byte aligned,
+ * and must not be shared by calls that may overlap. */
+int mla_decode_run(const mla_decode_ctx* ctx, const mla_decode_args* args, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* mla_decode_run, plus timing marks: records events[i] (hipEvent_t handles)
+ * on `stream` before launch i -- 0 split plan, 1 absorb product, 2 attention
+ * pass, 3 merge and W_UV product -- and events[4] after the last launch, so
+ * hipEventElapsedTime(events[i], events[i+1]) is kernel i's duration. NULL
+ * entries are skipped. For measurement tools; same arguments, errors and
+ * results as mla_decode_run. */
+int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* args,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const events[5]);
+
+/* Release a context (NULL is accepted). */
+void mla_decode_destroy(mla_decode_ctx* ctx);
+
+/* Static, human-readable text for a status code. */
+const char* mla_decode_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

@@ -1,0 +1,205 @@
+"""Thin ctypes binding of libmla_decode.so (include/mla_decode.h).
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels. PyTorch provides device memory and the current stream. The library
+must be built in-tree (``python -m mla_latent_kv_amd.build``); if it is
+missing, loading raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+MLA_OK = 0
+N_HEADS, D_NOPE, D_ROPE, D_LATENT, D_V, BLOCK = 128, 128, 64, 512, 128, 64
+
+
+class MlaDecodeConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_q_tokens", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("split_target", ctypes.c_int32),
+    ]
+
+
+class MlaDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_nope", ctypes.c_void_p),
+        ("q_pe", ctypes.c_void_p),
+        ("w_uk", ctypes.c_void_p),
+        ("w_uv", ctypes.c_void_p),
+        ("kv_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("batch", ctypes.c_int32),
+        ("q_tokens", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (once). Raises RuntimeError when it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mla_latent_kv_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    lib.mla_decode_init.argtypes = [ctypes.POINTER(MlaDecodeConfig), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_void_p)]
+    lib.mla_decode_init.restype = ctypes.c_int
+    lib.mla_decode_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_decode_workspace_size.restype = ctypes.c_int
+    lib.mla_decode_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaDecodeArgs),
+                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_decode_run.restype = ctypes.c_int
+    lib.mla_decode_run_profiled.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaDecodeArgs),
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_void_p)]
+    lib.mla_decode_run_profiled.restype = ctypes.c_int
+    lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
+    lib.mla_decode_destroy.restype = None
+    lib.mla_decode_status_string.argtypes = [ctypes.c_int]
+    lib.mla_decode_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def mla_decode_status_string(status: int) -> str:
+    return load_library().mla_decode_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != MLA_OK:
+        raise RuntimeError(f"{what}: {mla_decode_status_string(status)} ({status})")
+
+
+def mla_decode_init(device: int = 0, max_q_tokens: int = 2, softmax_scale: float = 0.0,
+                    split_target: int = 0, dims=None) -> ctypes.c_void_p:
+    """Create a context; ``dims`` overrides (H, d_nope, d_rope, d_latent, d_v, block)."""
+    h, dn, dr, dc, dv, bs = dims or (N_HEADS, D_NOPE, D_ROPE, D_LATENT, D_V, BLOCK)
+    cfg = MlaDecodeConfig(h, dn, dr, dc, dv, bs, max_q_tokens, float(softmax_scale),
+                          int(split_target))
+    ctx = ctypes.c_void_p()
+    _check(load_library().mla_decode_init(ctypes.byref(cfg), int(device), ctypes.byref(ctx)),
+           "mla_decode_init")
+    return ctx
+
+
+def mla_decode_workspace_size(ctx, batch: int, q_tokens: int, max_seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mla_decode_workspace_size(ctx, int(batch), int(q_tokens),
+                                                    int(max_seq_len), ctypes.byref(n)),
+           "mla_decode_workspace_size")
+    return n.value
+
+
+def mla_decode_destroy(ctx) -> None:
+    if ctx:
+        load_library().mla_decode_destroy(ctx)
+
+
+def _require(t, name, dtypes, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
+
+
+def mla_decode_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_lens,
+                   max_seq_len: int, out=None, workspace=None, stream=None):
+    """Enqueue one decode step; returns ``out`` (fp32 [B, Sq, 128, 128]).
+
+    bf16 tensors may be torch.bfloat16 or 16-bit integer views of the same bits.
+    ``workspace``: a uint8 CUDA tensor of at least mla_decode_workspace_size bytes
+    (allocated here when None). ``stream``: a torch.cuda.Stream or None for the
+    current stream.
+    """
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _require(q_nope, "q_nope", b16, 4)
+    _require(q_pe, "q_pe", b16, 4)
+    _require(w_uk, "w_uk", b16, 3)
+    _require(w_uv, "w_uv", b16, 3)
+    _require(kv_cache, "kv_cache", b16, 3)
+    _require(block_table, "block_table", (torch.int32,), 2)
+    _require(seq_lens, "seq_lens", (torch.int32,), 1)
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    if tuple(q_nope.shape[2:]) != (N_HEADS, D_NOPE) or tuple(q_pe.shape) != (B, Sq, N_HEADS, D_ROPE):
+        raise ValueError("q_nope / q_pe shapes must be [B, Sq, 128, 128] / [B, Sq, 128, 64]")
+    if tuple(w_uk.shape) != (N_HEADS, D_NOPE, D_LATENT) or tuple(w_uv.shape) != (N_HEADS, D_V, D_LATENT):
+        raise ValueError("w_uk / w_uv must be [128, 128, 512]")
+    if tuple(kv_cache.shape[1:]) != (BLOCK, D_LATENT + D_ROPE):
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table / seq_lens batch mismatch")
+    if out is None:
+        out = torch.empty((B, Sq, N_HEADS, D_V), dtype=torch.float32, device=q_nope.device)
+    _require(out, "out", (torch.float32,), 4)
+    if tuple(out.shape) != (B, Sq, N_HEADS, D_V):
+        raise ValueError("out must be [B, Sq, 128, 128] fp32")
+    need = mla_decode_workspace_size(ctx, B, Sq, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    s = stream if stream is not None else torch.cuda.current_stream(q_nope.device)
+    args = MlaDecodeArgs(
+        q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+        kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+        kv_cache.shape[0], B, Sq, block_table.shape[1], int(max_seq_len))
+    _check(load_library().mla_decode_run(ctx, ctypes.byref(args), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         ctypes.c_void_p(s.cuda_stream)),
+           "mla_decode_run")
+    return out
+
+
+class MLADecoder:
+    """Owns a context; ``decoder(...)`` forwards to mla_decode_run."""
+
+    def __init__(self, device: int = 0, max_q_tokens: int = 2, softmax_scale: float = 0.0,
+                 split_target: int = 0):
+        self.device = device
+        self.ctx = mla_decode_init(device, max_q_tokens, softmax_scale, split_target)
+
+    def workspace_size(self, batch, q_tokens, max_seq_len) -> int:
+        return mla_decode_workspace_size(self.ctx, batch, q_tokens, max_seq_len)
+
+    def __call__(self, *args, **kw):
+        return mla_decode_run(self.ctx, *args, **kw)
+
+    def close(self):
+        if self.ctx:
+            mla_decode_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,172 @@
+// C ABI of the MLA decode library (declared in include/mla_decode.h):
+// argument validation, workspace sizing and the launch sequence
+// plan -> absorb -> attention -> merge, all on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/mla_decode.h"
+#include "common.h"
+
+struct mla_decode_ctx {
+  mla_decode_config cfg;
+  int device;
+  int n_cu;
+  float scale;
+  int split_target;   // 0 = default for the device
+};
+
+namespace {
+int split_target_of(const mla_decode_ctx* c, int q_tokens) {
+  return c->split_target > 0 ? c->split_target : mla::default_split_target(c->n_cu, q_tokens);
+}
+}  // namespace
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_decode_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration or device";
+    case MLA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_decode_init(const mla_decode_config* cfg, int hip_device, mla_decode_ctx** out) {
+  if (!cfg || !out) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (cfg->num_heads != mla::kHeads || cfg->d_nope != mla::kDNope || cfg->d_rope != mla::kDRope ||
+      cfg->d_latent != mla::kDLat || cfg->d_v != mla::kDV || cfg->block_size != mla::kBlock)
+    return MLA_ERR_UNSUPPORTED;
+  if (cfg->max_q_tokens < 1 || cfg->max_q_tokens > 2) return MLA_ERR_UNSUPPORTED;
+  if (!(cfg->softmax_scale == cfg->softmax_scale)) return MLA_ERR_INVALID_ARG;   // NaN
+  if (cfg->split_target < 0 || cfg->split_target > (1 << 20)) return MLA_ERR_INVALID_ARG;
+  int n_dev = 0;
+  if (hipGetDeviceCount(&n_dev) != hipSuccess) return MLA_ERR_HIP;
+  if (hip_device < 0 || hip_device >= n_dev) return MLA_ERR_INVALID_ARG;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, hip_device) != hipSuccess) return MLA_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MLA_ERR_UNSUPPORTED;
+  mla_decode_ctx* c = new (std::nothrow) mla_decode_ctx;
+  if (!c) return MLA_ERR_INVALID_ARG;
+  c->cfg = *cfg;
+  c->device = hip_device;
+  c->n_cu = prop.multiProcessorCount;
+  c->split_target = cfg->split_target;
+  c->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale
+                                      : 1.0f / sqrtf((float)(cfg->d_nope + cfg->d_rope));
+  *out = c;
+  return MLA_OK;
+}
+
+int mla_decode_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                              int32_t max_seq_len, size_t* bytes) {
+  if (!ctx || !bytes || batch < 1 || max_seq_len < 1) return MLA_ERR_INVALID_ARG;
+  if (q_tokens < 1 || q_tokens > ctx->cfg.max_q_tokens) return MLA_ERR_INVALID_ARG;
+  const mla::Layout L =
+      mla::make_layout(batch, q_tokens, max_seq_len, split_target_of(ctx, q_tokens));
+  *bytes = L.total;
+  return MLA_OK;
+}
+
+namespace {
+
+int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspace,
+             size_t workspace_bytes, void* stream_handle, void* const* events) {
+  if (!ctx || !a) return MLA_ERR_INVALID_ARG;
+  if (!a->q_nope || !a->q_pe || !a->w_uk || !a->w_uv || !a->kv_cache || !a->block_table ||
+      !a->seq_lens || !a->out)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->q_tokens < 1 || a->q_tokens > ctx->cfg.max_q_tokens ||
+      a->num_blocks < 1 || a->max_blocks_per_seq < 1 || a->max_seq_len < 1)
+    return MLA_ERR_INVALID_ARG;
+  if ((long long)a->max_blocks_per_seq * mla::kBlock < a->max_seq_len) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(a->q_nope) || !aligned16(a->q_pe) || !aligned16(a->w_uk) ||
+      !aligned16(a->w_uv) || !aligned16(a->kv_cache) || !aligned16(a->block_table) ||
+      !aligned16(a->seq_lens) || !aligned16(a->out))
+    return MLA_ERR_MISALIGNED;
+  const int target = split_target_of(ctx, a->q_tokens);
+  const mla::Layout L = mla::make_layout(a->batch, a->q_tokens, a->max_seq_len, target);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total)
+    return MLA_ERR_WORKSPACE;
+
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+
+  char* ws = (char*)workspace;
+  mla::WorkItem* work = (mla::WorkItem*)(ws + L.work);
+  mla::SeqInfo* seqinfo = (mla::SeqInfo*)(ws + L.seqinfo);
+  int* meta = (int*)(ws + L.meta);
+  _Float16* q_abs = (_Float16*)(ws + L.qabs);
+  float* part_o = (float*)(ws + L.part_o);
+  float* part_ml = (float*)(ws + L.part_ml);
+  const int max_len = (int)((long long)a->max_blocks_per_seq * mla::kBlock < a->max_seq_len
+                                ? (long long)a->max_blocks_per_seq * mla::kBlock
+                                : a->max_seq_len);
+
+  auto mark = [&](int i) -> bool {
+    return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], stream) == hipSuccess;
+  };
+  int status = MLA_OK;
+  if (!mark(0) ||
+      mla::launch_plan(a->seq_lens, a->batch, max_len, target, L.max_chunks, work, seqinfo, meta,
+                       stream) != hipSuccess ||
+      !mark(1) ||
+      mla::launch_absorb((const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,
+                         stream) != hipSuccess) {
+    status = MLA_ERR_HIP;
+  } else {
+    mla::AttnArgs aa;
+    aa.cache = (const uint16_t*)a->kv_cache;
+    aa.block_table = a->block_table;
+    aa.q_pe = (const uint16_t*)a->q_pe;
+    aa.q_abs = q_abs;
+    aa.work = work;
+    aa.seqinfo = seqinfo;
+    aa.meta = meta;
+    aa.part_o = part_o;
+    aa.part_ml = part_ml;
+    aa.num_blocks = a->num_blocks;
+    aa.max_blocks_per_seq = a->max_blocks_per_seq;
+    aa.q_tokens = a->q_tokens;
+    aa.max_chunks = L.max_chunks;
+    aa.scale_log2 = ctx->scale * 1.4426950408889634f;
+    if (!mark(2) || mla::launch_attn(aa, stream) != hipSuccess || !mark(3) ||
+        mla::launch_merge(part_o, part_ml, seqinfo, (const uint16_t*)a->w_uv, a->out, a->batch,
+                          a->q_tokens, stream) != hipSuccess ||
+        !mark(4))
+      status = MLA_ERR_HIP;
+  }
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
+}
+
+}  // namespace
+
+int mla_decode_run(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return run_impl(ctx, a, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* a,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const events[5]) {
+  return run_impl(ctx, a, workspace, workspace_bytes, stream, events);
+}
+
+void mla_decode_destroy(mla_decode_ctx* ctx) { delete ctx; }
+
+}  // extern "C"

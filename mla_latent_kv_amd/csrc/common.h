@@ -1,0 +1,112 @@
+// Shared definitions of the gfx950 MLA decode kernels: fixed dimensions,
+// vector types, the workspace layout and the launchers each kernel file
+// provides to the C ABI in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// DeepSeek-V3 MLA dimensions ("DeepSeek-V3" page, configuration table).
+constexpr int kHeads = 128;
+constexpr int kDNope = 128;
+constexpr int kDRope = 64;
+constexpr int kDLat = 512;
+constexpr int kDV = 128;
+constexpr int kRow = kDLat + kDRope;    // 576 cached elements per token
+constexpr int kRowBytes = kRow * 2;     // 1152
+constexpr int kBlock = 64;              // tokens per cache block
+
+// Work decomposition of the attention pass.
+constexpr int kTileTok = 32;            // cached tokens per LDS tile
+constexpr int kRowsPerWave = 32;        // query rows (heads) per wavefront
+constexpr int kWaves = 4;               // wavefronts per workgroup
+constexpr int kRowsPerWg = kRowsPerWave * kWaves;   // 128
+constexpr int kMinChunk = 64;           // split granularity (one cache block)
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// One split of one sequence: tokens [t_begin, t_end) of sequence b; its
+// partial softmax state goes to slot `slot`.
+struct WorkItem {
+  int b, t_begin, t_end, slot;
+};
+
+// Per-sequence split summary written by the plan kernel: partial slots
+// [base, base + count), and the effective length used by every kernel.
+struct SeqInfo {
+  int base, count, len, pad;
+};
+
+// Byte offsets of each region inside the caller's workspace.
+struct Layout {
+  size_t work, seqinfo, meta, qabs, part_o, part_ml, total;
+  int max_chunks;   // capacity of the work list / partial slots
+  int rows;         // B * Sq query rows
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Split target: the plan aims for about this many chunks (workgroups for
+// Sq = 1; each chunk is two workgroups for Sq = 2).
+inline int default_split_target(int n_cu, int q_tokens) {
+  return q_tokens == 1 ? n_cu : n_cu / 2;
+}
+
+inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_target) {
+  Layout L{};
+  const int max_blocks = (max_seq_len + kBlock - 1) / kBlock;
+  long long cap = (long long)split_target + batch;   // sum_b ceil(L_b / C) <= total/C + B
+  long long by_len = (long long)batch * max_blocks;  // chunks are >= one block
+  L.max_chunks = (int)(cap < by_len ? cap : by_len);
+  if (L.max_chunks < 1) L.max_chunks = 1;
+  L.rows = batch * q_tokens;
+  const size_t rows_per_chunk = (size_t)q_tokens * kHeads;
+  size_t off = 0;
+  L.work = off;    off = align_up(off + sizeof(WorkItem) * L.max_chunks, 256);
+  L.seqinfo = off; off = align_up(off + sizeof(SeqInfo) * batch, 256);
+  L.meta = off;    off = align_up(off + 64, 256);
+  L.qabs = off;    off = align_up(off + (size_t)L.rows * kHeads * kDLat * 2, 256);
+  L.part_o = off;  off = align_up(off + (size_t)L.max_chunks * rows_per_chunk * kDLat * 4, 256);
+  L.part_ml = off; off = align_up(off + (size_t)L.max_chunks * rows_per_chunk * 2 * 4, 256);
+  L.total = off;
+  return L;
+}
+
+// ---- launchers (each returns hipGetLastError() of its launch)
+hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_len, int split_target,
+                       int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
+                       hipStream_t stream);
+hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
+                         hipStream_t stream);
+struct AttnArgs {
+  const uint16_t* cache;
+  const int32_t* block_table;
+  const uint16_t* q_pe;
+  const _Float16* q_abs;
+  const WorkItem* work;
+  const SeqInfo* seqinfo;
+  const int* meta;
+  float* part_o;
+  float* part_ml;
+  long long num_blocks;
+  int max_blocks_per_seq;
+  int q_tokens;
+  int max_chunks;
+  float scale_log2;   // softmax scale * log2(e)
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_merge(const float* part_o, const float* part_ml, const SeqInfo* seqinfo,
+                        const uint16_t* w_uv, float* out, int batch, int q_tokens,
+                        hipStream_t stream);
+
+}  // namespace mla
