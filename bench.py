@@ -178,10 +178,11 @@ def main() -> int:
         if rc != 0:
             raise RuntimeError(binding.mla_decode_status_string(rc))
     torch.cuda.synchronize()
-    names = ["plan", "absorb", "attention", "merge"]
-    kern_ms = {n: 0.0 for n in names}
+    # stage boundaries: 1 -> 2 plan + absorb (prep), 2 -> 3 attention, 3 -> 4 merge + W_UV
+    names = {1: "prep", 2: "attention", 3: "merge"}
+    kern_ms = {n: 0.0 for n in names.values()}
     for i in range(n_prof):
-        for j, n in enumerate(names):
+        for j, n in names.items():
             kern_ms[n] += _elapsed(hip, evs[5 * i + j], evs[5 * i + j + 1]) / n_prof
     for e in evs:
         hip.hipEventDestroy(e)

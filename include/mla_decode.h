@@ -97,7 +97,7 @@ typedef struct mla_decode_args {
   const int32_t* seq_lens;    /* int32 [B] */
   float* out;                 /* fp32 [B, Sq, H, 128] */
   int64_t num_blocks;         /* blocks in kv_cache */
-  int32_t batch;              /* B >= 1 */
+  int32_t batch;              /* 1 <= B <= 1000000 */
   int32_t q_tokens;           /* Sq: 1 or 2, <= max_q_tokens */
   int32_t max_blocks_per_seq; /* row stride of block_table */
   int32_t max_seq_len;        /* host upper bound on every L_b;
@@ -126,12 +126,13 @@ int mla_decode_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t 
 int mla_decode_run(const mla_decode_ctx* ctx, const mla_decode_args* args, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* mla_decode_run, plus timing marks: records events[i] (hipEvent_t handles)
- * on `stream` before launch i -- 0 split plan, 1 absorb product, 2 attention
- * pass, 3 merge and W_UV product -- and events[4] after the last launch, so
- * hipEventElapsedTime(events[i], events[i+1]) is kernel i's duration. NULL
- * entries are skipped. For measurement tools; same arguments, errors and
- * results as mla_decode_run. */
+/* mla_decode_run, plus timing marks for measurement tools: records the
+ * hipEvent_t handles events[0] and events[1] before the preparation launch
+ * (split plan and absorb product), events[2] before the attention pass,
+ * events[3] before the merge and W_UV product and events[4] after it, so
+ * hipEventElapsedTime(events[i], events[i+1]) is a stage's duration (stage 0
+ * is empty). NULL entries are skipped. Same arguments, errors and results as
+ * mla_decode_run. */
 int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* args,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]);

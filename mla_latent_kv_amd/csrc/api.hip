@@ -51,7 +51,7 @@ int mla_decode_init(const mla_decode_config* cfg, int hip_device, mla_decode_ctx
     return MLA_ERR_UNSUPPORTED;
   if (cfg->max_q_tokens < 1 || cfg->max_q_tokens > 2) return MLA_ERR_UNSUPPORTED;
   if (!(cfg->softmax_scale == cfg->softmax_scale)) return MLA_ERR_INVALID_ARG;   // NaN
-  if (cfg->split_target < 0 || cfg->split_target > (1 << 20)) return MLA_ERR_INVALID_ARG;
+  if (cfg->split_target < 0 || cfg->split_target > mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
   int n_dev = 0;
   if (hipGetDeviceCount(&n_dev) != hipSuccess) return MLA_ERR_HIP;
   if (hip_device < 0 || hip_device >= n_dev) return MLA_ERR_INVALID_ARG;
@@ -72,7 +72,8 @@ int mla_decode_init(const mla_decode_config* cfg, int hip_device, mla_decode_ctx
 
 int mla_decode_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
                               int32_t max_seq_len, size_t* bytes) {
-  if (!ctx || !bytes || batch < 1 || max_seq_len < 1) return MLA_ERR_INVALID_ARG;
+  if (!ctx || !bytes || batch < 1 || batch > mla::kMaxBatch || max_seq_len < 1)
+    return MLA_ERR_INVALID_ARG;
   if (q_tokens < 1 || q_tokens > ctx->cfg.max_q_tokens) return MLA_ERR_INVALID_ARG;
   const mla::Layout L =
       mla::make_layout(batch, q_tokens, max_seq_len, split_target_of(ctx, q_tokens));
@@ -88,7 +89,7 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
   if (!a->q_nope || !a->q_pe || !a->w_uk || !a->w_uv || !a->kv_cache || !a->block_table ||
       !a->seq_lens || !a->out)
     return MLA_ERR_INVALID_ARG;
-  if (a->batch < 1 || a->q_tokens < 1 || a->q_tokens > ctx->cfg.max_q_tokens ||
+  if (a->batch < 1 || a->batch > mla::kMaxBatch || a->q_tokens < 1 || a->q_tokens > ctx->cfg.max_q_tokens ||
       a->num_blocks < 1 || a->max_blocks_per_seq < 1 || a->max_seq_len < 1)
     return MLA_ERR_INVALID_ARG;
   if ((long long)a->max_blocks_per_seq * mla::kBlock < a->max_seq_len) return MLA_ERR_INVALID_ARG;
@@ -111,8 +112,8 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
   mla::SeqInfo* seqinfo = (mla::SeqInfo*)(ws + L.seqinfo);
   int* meta = (int*)(ws + L.meta);
   _Float16* q_abs = (_Float16*)(ws + L.qabs);
-  float* part_o = (float*)(ws + L.part_o);
-  float* part_ml = (float*)(ws + L.part_ml);
+  _Float16* part_o = (_Float16*)(ws + L.part_o);
+  float* part_lse = (float*)(ws + L.part_lse);
   const int max_len = (int)((long long)a->max_blocks_per_seq * mla::kBlock < a->max_seq_len
                                 ? (long long)a->max_blocks_per_seq * mla::kBlock
                                 : a->max_seq_len);
@@ -121,12 +122,10 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
     return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], stream) == hipSuccess;
   };
   int status = MLA_OK;
-  if (!mark(0) ||
-      mla::launch_plan(a->seq_lens, a->batch, max_len, target, L.max_chunks, work, seqinfo, meta,
-                       stream) != hipSuccess ||
-      !mark(1) ||
-      mla::launch_absorb((const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,
-                         stream) != hipSuccess) {
+  if (!mark(0) || !mark(1) ||
+      mla::launch_prep(a->seq_lens, a->batch, max_len, target, L.max_chunks, work, seqinfo, meta,
+                       (const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,
+                       stream) != hipSuccess) {
     status = MLA_ERR_HIP;
   } else {
     mla::AttnArgs aa;
@@ -138,14 +137,14 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
     aa.seqinfo = seqinfo;
     aa.meta = meta;
     aa.part_o = part_o;
-    aa.part_ml = part_ml;
+    aa.part_lse = part_lse;
     aa.num_blocks = a->num_blocks;
     aa.max_blocks_per_seq = a->max_blocks_per_seq;
     aa.q_tokens = a->q_tokens;
     aa.max_chunks = L.max_chunks;
     aa.scale_log2 = ctx->scale * 1.4426950408889634f;
     if (!mark(2) || mla::launch_attn(aa, stream) != hipSuccess || !mark(3) ||
-        mla::launch_merge(part_o, part_ml, seqinfo, (const uint16_t*)a->w_uv, a->out, a->batch,
+        mla::launch_merge(part_o, part_lse, seqinfo, (const uint16_t*)a->w_uv, a->out, a->batch,
                           a->q_tokens, stream) != hipSuccess ||
         !mark(4))
       status = MLA_ERR_HIP;

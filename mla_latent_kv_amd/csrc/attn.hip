@@ -4,7 +4,8 @@
 // rows, stream the 576-wide cached rows through LDS once and compute, per row:
 //   s_j  = scale * (q_abs . c_KV,j + q_pe . k_R,j)
 //   running max m, running sum l, O = sum_j exp(s_j - m) c_KV,j   (512 wide)
-// then write the partial state (O, m, l) for the merge pass. This is the absorb
+// then write the normalised partial O / l (fp16) and lse = m + log2 l for the
+// merge pass. This is the absorb
 // order of the "DeepSeek-V3" page (ailearn.mscapital.top), MLA section: the
 // query side already carries W_UK, the RoPE part is multiplied separately and
 // added, and the latent is aggregated before W_UV, so per-head keys and values
@@ -52,7 +53,9 @@ constexpr int kThreads = kWaves * 64;                     // 256
 constexpr int kFetch = kTileBytes / 16 / kThreads;        // 9 granules per lane per tile
 constexpr int kNBuf = 3;                                  // LDS tile ring
 constexpr int kQpWaveBytes = kRowsPerWave * kDRope * 2;   // 4 KB of q_pe per wavefront
-constexpr int kLdsBytes = kNBuf * kTileBytes + kWaves * kQpWaveBytes;
+constexpr int kRingBytes = kNBuf * kTileBytes + kWaves * kQpWaveBytes;
+constexpr int kEpiBytes = kWaves * kRowsPerWave * kDLat * 2;   // fp16 transpose space
+constexpr int kLdsBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
 constexpr float kRescaleLog2 = 8.0f;                      // lazy max threshold
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
@@ -252,44 +255,52 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[ks], br[ks], s, 0, 0, 0);
     }
 
-    // -- online softmax (log2 domain); s[i] is token 8 (i/4) + 4 half + i%4
-    float mt = -INFINITY;
+    // -- online softmax in log2 units: m is the running reference (scaled),
+    // p = 2^(s * scale * log2 e - m). s[i] is token 8 (i/4) + 4 half + i%4.
+    // Masking is needed only on a split's last tile or a query's last visible one.
+    if (ts + kTileTok > lim) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = ts + 8 * (i >> 2) + 4 * half + (i & 3);
-      s[i] = tok < lim ? s[i] * p.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, s[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int tok = ts + 8 * (i >> 2) + 4 * half + (i & 3);
+        s[i] = tok < lim ? s[i] : -INFINITY;
+      }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                         fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
     const bool grow = mt > m + kRescaleLog2;
     if (__any(grow)) {
       const float m_new = grow ? mt : m;
-      const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - m_new);
-      l *= alpha;
-      // O *= alpha in place in the accumulator registers (one read / multiply /
-      // write per element, so O never leaves the AGPRs); the s_nops cover the
-      // MFMA -> accumulator-read and write -> MFMA dependency distances.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      if (__any(grow && m != -INFINITY)) {
+        // O *= 2^(m - m_new) in place in the accumulator registers (one read /
+        // multiply / write per element, so O never leaves the AGPRs); the
+        // s_nops cover the MFMA -> accumulator-read and write -> MFMA distances.
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-      for (int c = 0; c < 16; ++c)
+        for (int c = 0; c < 16; ++c)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = o[c][i], tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-              : "+a"(x), "=&v"(tmp)
-              : "v"(alpha));
-          o[c][i] = x;
-        }
-      asm volatile("s_nop 7" ::: "memory");
+          for (int i = 0; i < 16; ++i) {
+            float x = o[c][i], tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha));
+            o[c][i] = x;
+          }
+        asm volatile("s_nop 7" ::: "memory");
+      }
       m = m_new;
     }
-    const float m_use = (m == -INFINITY) ? 0.f : m;
+    const float neg_m = (m == -INFINITY) ? 0.f : -m;
     float rs = 0.f;
     f16x8 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float e = exp2f(s[i] - m_use);
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, neg_m));
       rs += e;
       pb[i >> 3][i & 7] = (_Float16)e;
     }
@@ -332,21 +343,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     cur_i = nxt_i;
   }
 
-  // ---- partial state: O rows are (qi, head), 512 fp32 each
-  const int prow = qi * kHeads + hg * 32 + l32;
-  const size_t rows_per_chunk = (size_t)p.q_tokens * kHeads;
-  float* dst = p.part_o + ((size_t)wi.slot * rows_per_chunk + prow) * kDLat;
+  // ---- partial state: o_hat = O / l rounded to fp16 (the merge only needs
+  // the normalised partial and lse = m + log2 l), rows (qi, head) of 512
+  // contiguous values. The accumulator layout (lane = head, registers =
+  // columns) is turned head-major through this wave's 32 KB of LDS (the tile
+  // ring is free after the last barrier): 8-byte column units, unit index
+  // XOR 2 (head % 16) so rows of equal bank phase spread over the banks.
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const float lse = l > 0.f ? m + __log2f(l) : -INFINITY;
+  char* tw = smem + w * (kRowsPerWave * kDLat * 2);
+  const int xr = 2 * (l32 & 15);
 #pragma unroll
   for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int col = 32 * ct + 8 * q + 4 * half;
-      *(f32x4*)(dst + col) = f32x4{o[ct][4 * q], o[ct][4 * q + 1], o[ct][4 * q + 2], o[ct][4 * q + 3]};
+      const int u = 8 * ct + 2 * q + half;   // 4-column unit of columns 32 ct + 8 q + 4 half
+      f16x4 v = {(_Float16)(o[ct][4 * q] * inv_l), (_Float16)(o[ct][4 * q + 1] * inv_l),
+                 (_Float16)(o[ct][4 * q + 2] * inv_l), (_Float16)(o[ct][4 * q + 3] * inv_l)};
+      *(f16x4*)(tw + l32 * (kDLat * 2) + 8 * (u ^ xr)) = v;
     }
-  if (half == 0) {
-    float* ml = p.part_ml + ((size_t)wi.slot * rows_per_chunk + prow) * 2;
-    ml[0] = m;
-    ml[1] = l;
+  const size_t rows_per_chunk = (size_t)p.q_tokens * kHeads;
+  const size_t row0 = (size_t)wi.slot * rows_per_chunk + qi * kHeads + hg * 32;
+  if (half == 0) p.part_lse[row0 + l32] = lse;
+  MLA_WAIT_LGKM0();   // this wave's own LDS writes only: no barrier needed
+  _Float16* dst = p.part_o + row0 * kDLat;
+#pragma unroll 8
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int xj = 2 * (j & 15);
+    const u32x4 v = *(const u32x4*)(tw + j * (kDLat * 2) + 8 * ((2 * lane) ^ xj));
+    *(u32x4*)(dst + (size_t)j * kDLat + 8 * lane) = v;
   }
 }
 

@@ -25,6 +25,7 @@ constexpr int kRowsPerWave = 32;        // query rows (heads) per wavefront
 constexpr int kWaves = 4;               // wavefronts per workgroup
 constexpr int kRowsPerWg = kRowsPerWave * kWaves;   // 128
 constexpr int kMinChunk = 64;           // split granularity (one cache block)
+constexpr int kMaxBatch = 1000000;      // keeps the plan's packed 21-bit counters exact
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -49,7 +50,7 @@ struct SeqInfo {
 
 // Byte offsets of each region inside the caller's workspace.
 struct Layout {
-  size_t work, seqinfo, meta, qabs, part_o, part_ml, total;
+  size_t work, seqinfo, meta, qabs, part_o, part_lse, total;
   int max_chunks;   // capacity of the work list / partial slots
   int rows;         // B * Sq query rows
 };
@@ -76,18 +77,18 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
   L.seqinfo = off; off = align_up(off + sizeof(SeqInfo) * batch, 256);
   L.meta = off;    off = align_up(off + 64, 256);
   L.qabs = off;    off = align_up(off + (size_t)L.rows * kHeads * kDLat * 2, 256);
-  L.part_o = off;  off = align_up(off + (size_t)L.max_chunks * rows_per_chunk * kDLat * 4, 256);
-  L.part_ml = off; off = align_up(off + (size_t)L.max_chunks * rows_per_chunk * 2 * 4, 256);
+  L.part_o = off;   off = align_up(off + (size_t)L.max_chunks * rows_per_chunk * kDLat * 2, 256);
+  L.part_lse = off; off = align_up(off + (size_t)L.max_chunks * rows_per_chunk * 4, 256);
   L.total = off;
   return L;
 }
 
 // ---- launchers (each returns hipGetLastError() of its launch)
-hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_len, int split_target,
+// split plan + absorb product (one launch)
+hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target,
                        int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
+                       const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
                        hipStream_t stream);
-hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
-                         hipStream_t stream);
 struct AttnArgs {
   const uint16_t* cache;
   const int32_t* block_table;
@@ -96,8 +97,8 @@ struct AttnArgs {
   const WorkItem* work;
   const SeqInfo* seqinfo;
   const int* meta;
-  float* part_o;
-  float* part_ml;
+  _Float16* part_o;   // [slot][Sq * 128 rows][512] normalised partial O
+  float* part_lse;    // [slot][Sq * 128 rows] m + log2 l (log2 units), -inf if empty
   long long num_blocks;
   int max_blocks_per_seq;
   int q_tokens;
@@ -105,7 +106,7 @@ struct AttnArgs {
   float scale_log2;   // softmax scale * log2(e)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_merge(const float* part_o, const float* part_ml, const SeqInfo* seqinfo,
+hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const SeqInfo* seqinfo,
                         const uint16_t* w_uv, float* out, int batch, int q_tokens,
                         hipStream_t stream);
 
