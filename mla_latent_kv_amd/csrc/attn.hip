@@ -41,6 +41,12 @@
 //   -inf with a select). A granule swizzle g ^ f(row) keeps the score reads,
 //   the transposed reads and the conversion pass free of bank conflicts; the
 //   fetch addresses apply the inverse permutation.
+// * per tile, one barrier: scores (36 MFMAs); row max and the first half of
+//   the exponentials; then the P.C product in two 16-token halves, the second
+//   half's exponentials and the conversion of the next tile running on the
+//   VALU/LDS under the first half's MFMAs. The score chain accumulates in VGPRs
+//   (issued as inline MFMAs, the result-to-VALU distance covered by s_nop) so
+//   that O owns all 256 accumulator registers.
 #include "common.h"
 
 namespace mla {
@@ -56,10 +62,9 @@ constexpr int kQpWaveBytes = kRowsPerWave * kDRope * 2;   // 4 KB of q_pe per wa
 constexpr int kRingBytes = kNBuf * kTileBytes + kWaves * kQpWaveBytes;
 constexpr int kEpiBytes = kWaves * kRowsPerWave * kDLat * 2;   // fp16 transpose space
 constexpr int kLdsBytes = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
-constexpr float kRescaleLog2 = 8.0f;                      // lazy max threshold
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+constexpr float kRescaleLog2 = 15.0f;                     // lazy max threshold (p < 2^15 in fp16)
 
-// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8; an all-ones field means "do not wait on this counter".
 #define MLA_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 #define MLA_WAIT_LGKM0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 #define MLA_BARRIER() asm volatile("s_barrier" ::: "memory")
@@ -94,6 +99,43 @@ __device__ __forceinline__ f16x8 lds_read_tr(const char* p0, const char* p1) {
   return __builtin_bit_cast(f16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Scores of one tile: D[token, head] over 32 fp16 k-steps (latent) and 4 bf16
+// k-steps (RoPE). Accumulates in VGPRs: dependent MFMAs on one accumulator
+// issue back to back; s_nop 15 covers the MFMA-result -> VALU-read distance.
+// fetch(j), j = 0..8, is called after every fourth MFMA so that the next
+// tile's direct-to-LDS loads issue under the matrix work instead of in a burst.
+template <typename Fetch>
+__device__ __forceinline__ f32x16 score_tile(const char* cur, const int (&s_off)[4],
+                                             const f16x8 (&qa)[32], const char* qp_row,
+                                             int qp_x, Fetch&& fetch) {
+  constexpr int kPre = 4;
+  f16x8 a[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) a[j] = lds_read16<f16x8>(cur, s_off[j & 3] + 128 * (j >> 2));
+  f32x16 s;
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=v"(s) : "v"(a[0]), "v"(qa[0]));
+  fetch(0);
+  a[0] = lds_read16<f16x8>(cur, s_off[0] + 128);
+#pragma unroll
+  for (int ks = 1; ks < 32; ++ks) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                 : "+v"(s)
+                 : "v"(a[ks % kPre]), "v"(qa[ks]));
+    if (ks % 4 == 0) fetch(ks / 4);
+    const int nk = ks + kPre;
+    if (nk < 32) a[ks % kPre] = lds_read16<f16x8>(cur, s_off[nk & 3] + 128 * (nk >> 2));
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 ar = lds_read16<bf16x8>(cur, s_off[ks] + 128 * 8);
+    const bf16x8 br = lds_read16<bf16x8>(qp_row, 16 * ((2 * ks + (qp_x >> 3)) ^ (qp_x & 7)));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ar), "v"(br));
+    if (ks == 0) fetch(8);
+  }
+  asm volatile("s_nop 15" : "+v"(s));
+  return s;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
@@ -125,37 +167,67 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   const int n_vis = L - p.q_tokens + qi + 1;                  // visible positions
   const int lim = min(wi.t_end, n_vis);                       // tokens this wave may use
 
-  // ---- fetch plan: wave w, fetch j moves LDS granule slots 256 j + 64 w + lane;
-  // slot P holds logical granule (P % 72) ^ swz(row) of row P / 72.
-  int plan[kFetch];   // byte offset in the global tile | row << 16 | is_c_kv << 23
-#pragma unroll
-  for (int j = 0; j < kFetch; ++j) {
-    const int P = kThreads * j + t;
-    const int row = P / kGranPerRow;
-    const int g = (P % kGranPerRow) ^ swz(row);
-    plan[j] = (row * kRowBytes + 16 * g) | (row << 16) | ((g < kDLat / 8) ? (1 << 23) : 0);
-  }
-  const int32_t* btab = p.block_table + (size_t)b * p.max_blocks_per_seq;
-  auto issue_tile = [&](int ts, char* buf) {
-    long long blk = btab[ts / kBlock];
-    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);   // memory safety
-    const char* src = (const char*)p.cache + ((size_t)blk * kBlock + (ts % kBlock)) * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < kFetch; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src + (plan[j] & 0xffff)),
-          (__attribute__((address_space(3))) void*)(buf + 1024 * (4 * j + w)), 16, 0, 0);
+  // ---- fetch plan: wave w, fetch j moves LDS granule slots P = 256 j + 64 w +
+  // lane; slot P holds logical granule (P % 72) ^ swz(row) of row P / 72
+  // (P / 72 == (P * 3641) >> 18 for P < 2304). Offsets are recomputed per use
+  // rather than held in registers.
+  int t_f = t;   // re-materialised each tile (see the loop) so offsets are not hoisted
+  auto slot_row = [&](int j) { return ((kThreads * j + t_f) * 3641) >> 18; };
+  auto fetch_off = [&](int j) {
+    const int P = kThreads * j + t_f, row = slot_row(j);
+    return row * kRowBytes + 16 * ((P - row * kGranPerRow) ^ swz(row));
   };
-  auto convert_tile = [&](char* buf, int ts) {
-    const int valid = wi.t_end - ts;   // rows of this tile inside the split
+  // block ids of this split, 64 per window: lane i holds the id of block
+  // blk_base + i; a tile reads its id with one lane read
+  const int32_t* btab = p.block_table + (size_t)b * p.max_blocks_per_seq;
+  const int blk_first = wi.t_begin / kBlock;
+  const int blk_last = (wi.t_end - 1) / kBlock;
+  int blk_base = blk_first;
+  int blk_lane = blk_first + lane <= blk_last ? btab[blk_first + lane] : 0;
+  // consume the load here, so no later wait on it can also drain the fetches
+  asm volatile("" : "+v"(blk_lane));
+  auto buf = [&](int i) -> char* { return smem + (i % kNBuf) * kTileBytes; };
+  // global address of the first row of the tile starting at token ts
+  auto tile_src = [&](int ts) -> const char* {
+    const int bi = ts / kBlock;
+    if (bi >= blk_base + 64) {   // next window (chunks longer than 4096 tokens)
+      blk_base += 64;
+      blk_lane = blk_base + lane <= blk_last ? btab[blk_base + lane] : 0;
+      asm volatile("" : "+v"(blk_lane));
+    }
+    long long blk = __builtin_amdgcn_readlane(blk_lane, bi - blk_base);
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);   // memory safety
+    return (const char*)p.cache + ((size_t)blk * kBlock + (ts % kBlock)) * kRowBytes;
+  };
+  // fetch j (of 9) of a tile into LDS buffer dst
+  auto fetch_one = [&](const char* src, char* dst, int j) {
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(src + (unsigned)fetch_off(j)),
+        (__attribute__((address_space(3))) void*)(dst + 1024 * (4 * j + w)), 16, 0, 0);
+  };
+  auto issue_tile = [&](int ts, char* dst) {
+    const char* src = tile_src(ts);
+#pragma unroll
+    for (int j = 0; j < kFetch; ++j) fetch_one(src, dst, j);
+  };
+  // in-place bf16 -> fp16 of the c_KV granules this lane fetched; rows past the
+  // split become zeros (k_R granules are rewritten unchanged). Reads first,
+  // then conversions, then writes, so the LDS latency is paid once.
+  auto convert_tile = [&](char* tb, int ts) {
+    const int valid = wi.t_end - ts;
+    u32x4 v[kFetch];
 #pragma unroll
     for (int j = 0; j < kFetch; ++j) {
-      if (plan[j] & (1 << 23)) {
-        u32x4* a = (u32x4*)(buf + 16 * (kThreads * j + t));
-        const int row = (plan[j] >> 16) & 31;
-        u32x4 v = *a;
-        *a = row < valid ? bf16x8_to_f16x8(v) : u32x4{0, 0, 0, 0};
-      }
+      const int row = slot_row(j);
+      if (kThreads * j + t - row * kGranPerRow < kDLat / 8)
+        v[j] = *(const u32x4*)(tb + 16 * (kThreads * j + t));
+    }
+#pragma unroll
+    for (int j = 0; j < kFetch; ++j) {
+      const int row = slot_row(j);
+      if (kThreads * j + t - row * kGranPerRow < kDLat / 8)
+        *(u32x4*)(tb + 16 * (kThreads * j + t)) =
+            row < valid ? bf16x8_to_f16x8(v[j]) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -176,6 +248,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       *(u32x4*)(qp_lds + row * 128 + 16 * (g ^ (row & 7))) = *(const u32x4*)(src + 8 * G);
     }
   }
+  const char* qp_row = qp_lds + l32 * 128;
+  const int qp_x = 8 * half + (l32 & 7);   // k-half of the B fragment, row swizzle
 
   // ---- per-lane LDS read offsets
   // scores: row = l32, logical granule 2 ks + half (+64 for k_R)
@@ -184,80 +258,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   for (int j = 0; j < 4; ++j) s_off[j] = l32 * kRowBytes + 16 * ((2 * j + half) ^ swz(l32));
   // transposed reads: group gg = lane / 16 (k-half hh = gg / 2, 16-col half
   // gg % 2), source lane L: token 16 st + 8 q + 4 hh + L / 4, column
-  // 32 ct + 16 (gg % 2) + 4 (L % 4). Offsets for ct = 0 and ct = 1; ct + 2
-  // adds one 128-byte block of 8 granules.
+  // 32 ct + 16 (gg % 2) + 4 (L % 4). swz(row) is the same for every (st, q),
+  // so two bases (ct parity) serve all reads; st, q and ct / 2 are immediates.
   const int gg = lane >> 4, Lq = lane & 15, hh = gg >> 1;
-  int tr_off[2][2][2];   // [st][q][ct parity]
+  int tr_off[2];
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = 16 * st + 8 * q + 4 * hh + (Lq >> 2);
-#pragma unroll
-      for (int cp = 0; cp < 2; ++cp) {
-        const int col = 32 * cp + 16 * (gg & 1) + 4 * (Lq & 3);
-        tr_off[st][q][cp] = row * kRowBytes + 16 * ((col >> 3) ^ swz(row)) + 2 * (col & 7);
-      }
-    }
-  const int qp_off = l32 * 128;
+  for (int cp = 0; cp < 2; ++cp) {
+    const int row = 4 * hh + (Lq >> 2);
+    const int col = 32 * cp + 16 * (gg & 1) + 4 * (Lq & 3);
+    tr_off[cp] = row * kRowBytes + 16 * ((col >> 3) ^ swz(row)) + 2 * (col & 7);
+  }
 
   f32x16 o[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) o[c] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 converted
-  const int n_tiles = (wi.t_end - wi.t_begin + kTileTok - 1) / kTileTok;
-  issue_tile(wi.t_begin, smem);
-  if (n_tiles > 1) {
-    issue_tile(wi.t_begin + kTileTok, smem + kTileBytes);
-    MLA_WAIT_VM(9);
-  } else {
-    MLA_WAIT_VM(0);
-  }
-  convert_tile(smem, wi.t_begin);
-  MLA_WAIT_LGKM0();
-  MLA_BARRIER();
-
-  int cur_i = 0;   // ring index of tile `it`
-  for (int it = 0; it < n_tiles; ++it) {
-    const int ts = wi.t_begin + it * kTileTok;
-    const int nxt_i = cur_i == kNBuf - 1 ? 0 : cur_i + 1;
-    const int far_i = nxt_i == kNBuf - 1 ? 0 : nxt_i + 1;
-    const bool far = it + 2 < n_tiles;
-    // tile it + 2 -> the buffer tile it - 1 used (every wave is past it)
-    if (far) issue_tile(ts + 2 * kTileTok, smem + far_i * kTileBytes);
-    const char* cur = smem + cur_i * kTileBytes;
-
-    // -- scores: 36 MFMAs; the A fragments are read from LDS kSPre steps ahead
-    // (sched_barrier keeps that order so LDS latency hides behind the MFMAs)
-    f32x16 s = {};
-    {
-      constexpr int kSPre = 4;
-      f16x8 a[kSPre];
-#pragma unroll
-      for (int j = 0; j < kSPre; ++j) a[j] = lds_read16<f16x8>(cur, s_off[j & 3] + 128 * (j >> 2));
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks % kSPre], qa[ks], s, 0, 0, 0);
-        const int nk = ks + kSPre;
-        if (nk < 32) a[ks % kSPre] = lds_read16<f16x8>(cur, s_off[nk & 3] + 128 * (nk >> 2));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      bf16x8 ar[4], br[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ar[ks] = lds_read16<bf16x8>(cur, s_off[ks] + 128 * 8);
-        br[ks] = lds_read16<bf16x8>(qp_lds, qp_off + 16 * ((2 * ks + half) ^ (l32 & 7)));
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[ks], br[ks], s, 0, 0, 0);
-    }
-
-    // -- online softmax in log2 units: m is the running reference (scaled),
-    // p = 2^(s * scale * log2 e - m). s[i] is token 8 (i/4) + 4 half + i%4.
-    // Masking is needed only on a split's last tile or a query's last visible one.
+  const float scale_log2 = p.scale_log2;
+  // Row max of the tile starting at token ts (raw scores s, masked in place)
+  // and the running reference m: moved (with O and l rescaled) only when the
+  // tile max exceeds it by more than 2^kRescaleLog2, so p stays below 2^15.
+  auto tile_max = [&](f32x16& s, int ts) {
+    // s[i] is token 8 (i/4) + 4 half + i%4 of the tile; masking only on a
+    // split's last tile or a query's last visible one
     if (ts + kTileTok > lim) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -269,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
                      fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                          fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
     const bool grow = mt > m + kRescaleLog2;
     if (__any(grow)) {
       const float m_new = grow ? mt : m;
@@ -295,53 +318,84 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       }
       m = m_new;
     }
+  };
+  // p = 2^(s * scale * log2 e - m) for tokens 16 h16 .. 16 h16 + 15 of the tile
+  // (registers 8 h16 .. 8 h16 + 7), packed as the B fragment of that half;
+  // returns their sum over the lane's 8 values
+  auto tile_exp = [&](const f32x16& s, int h16, f16x8& pbh) -> float {
     const float neg_m = (m == -INFINITY) ? 0.f : -m;
     float rs = 0.f;
-    f16x8 pb[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, neg_m));
+    for (int i = 0; i < 8; ++i) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h16 + i], scale_log2, neg_m));
       rs += e;
-      pb[i >> 3][i & 7] = (_Float16)e;
+      pbh[i] = (_Float16)e;
     }
-    rs += __shfl_xor(rs, 32);
-    l += rs;
-
-    // -- latent accumulation: o[ct] += C^T[32 ct .., tokens] * P^T, 32 MFMAs;
-    // transposed A fragments are read two MFMAs ahead
-    {
-      auto tr = [&](int idx) {
-        const int ct = idx >> 1, st = idx & 1;
-        const int blk = 128 * (ct >> 1);
-        return lds_read_tr(cur + tr_off[st][0][ct & 1] + blk, cur + tr_off[st][1][ct & 1] + blk);
-      };
-      constexpr int kPPre = 3;
-      f16x8 a[kPPre];
+    return rs;
+  };
+  // o[ct] += C^T[32 ct .., 16 tokens of half st] * P^T for the tile in `tb`:
+  // 16 MFMAs, the transposed A fragments read three MFMAs ahead
+  auto accumulate_half = [&](const char* tb, int st, const f16x8& pbh) {
+    auto tr = [&](int ct) {
+      const char* base = tb + tr_off[ct & 1] + 128 * (ct >> 1) + 16 * kRowBytes * st;
+      return lds_read_tr(base, base + 8 * kRowBytes);
+    };
+    constexpr int kPPre = 3;
+    f16x8 a[kPPre];
 #pragma unroll
-      for (int j = 0; j < kPPre; ++j) a[j] = tr(j);
+    for (int j = 0; j < kPPre; ++j) a[j] = tr(j);
 #pragma unroll
-      for (int idx = 0; idx < 32; ++idx) {
-        o[idx >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[idx % kPPre], pb[idx & 1], o[idx >> 1], 0, 0, 0);
-        if (idx + kPPre < 32) a[idx % kPPre] = tr(idx + kPPre);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int ct = 0; ct < 16; ++ct) {
+      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ct % kPPre], pbh, o[ct], 0, 0, 0);
+      if (ct + kPPre < 16) a[ct % kPPre] = tr(ct + kPPre);
     }
+  };
 
-    // -- tile it + 1 has landed (only tile it + 2's fetches may be pending):
-    // convert this lane's part of it, then one barrier publishes it and frees
-    // tile it's buffer for the fetch two tiles ahead.
-    if (it + 1 < n_tiles) {
+  // ---- prologue: tile 0 converted, tile 1 in flight
+  const int n_tiles = (wi.t_end - wi.t_begin + kTileTok - 1) / kTileTok;
+  const int t0 = wi.t_begin;
+  issue_tile(t0, buf(0));
+  if (n_tiles > 1) {
+    issue_tile(t0 + kTileTok, buf(1));
+    MLA_WAIT_VM(9);
+  } else {
+    MLA_WAIT_VM(0);
+  }
+  convert_tile(buf(0), t0);
+  MLA_WAIT_LGKM0();
+  MLA_BARRIER();
+
+  // ---- tile `it`: fetch tile it + 2 into the buffer tile it - 1 used, scores,
+  // softmax and accumulation of tile it, conversion of tile it + 1
+  for (int it = 0; it < n_tiles; ++it) {
+    asm volatile("" : "+v"(t_f));
+    const int ts = t0 + it * kTileTok;
+    const bool far = it + 2 < n_tiles, next = it + 1 < n_tiles;
+    const char* fsrc = far ? tile_src(ts + 2 * kTileTok) : nullptr;
+    char* fdst = buf(it + 2);
+    f32x16 s = score_tile(buf(it), s_off, qa, qp_row, qp_x, [&](int j) {
+      if (far) fetch_one(fsrc, fdst, j);
+    });
+    tile_max(s, ts);
+    f16x8 pb0, pb1;
+    float rs = tile_exp(s, 0, pb0);
+    if (next) {
       if (far) {
         MLA_WAIT_VM(9);
       } else {
         MLA_WAIT_VM(0);
       }
-      convert_tile(smem + nxt_i * kTileBytes, ts + kTileTok);
     }
+    accumulate_half(buf(it), 0, pb0);
+    rs += tile_exp(s, 1, pb1);
+    if (next) convert_tile(buf(it + 1), ts + kTileTok);
+    rs += __shfl_xor(rs, 32);
+    l += rs;
+    accumulate_half(buf(it), 1, pb1);
     MLA_WAIT_LGKM0();
     MLA_BARRIER();
-    cur_i = nxt_i;
   }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ---- partial state: o_hat = O / l rounded to fp16 (the merge only needs
   // the normalised partial and lse = m + log2 l), rows (qi, head) of 512
