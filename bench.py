@@ -37,6 +37,48 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 
+# HBM traffic of one attention launch from two rocprofv3 --pmc runs of this
+# script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+# the same counter reads for a plain device copy of known size (--copy-probe).
+# The figures belong to the attention source they were taken on: when the
+# source hash differs, traffic is reported as null.
+ATTN_TRAFFIC = {"src_sha256": "3d1e5de60918a42db2042ffe4e1682b2a0516a55f935d5ea9652280c331cd926",
+                "fetch_kib": 76202.619, "write_kib": 32896.0,
+                "fetch_scale": 1.99995, "write_scale": 1.0}
+TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def attn_traffic():
+    t = ATTN_TRAFFIC
+    if not t or t["src_sha256"] != attn_source_hash():
+        return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def copy_probe(mib: int) -> int:
+    """A plain device-to-device copy of `mib` MiB, five times: the calibration
+    kernel for the FETCH_SIZE / WRITE_SIZE counters (reads and writes exactly
+    mib MiB per dispatch)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}), flush=True)
+    return 0
+
 
 def _hip():
     lib = ctypes.CDLL("libamdhip64.so")
@@ -100,7 +142,11 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               "requested). Sequences shard across GPUs with no exchange; run one process "
@@ -219,7 +265,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": attn_traffic(),
             "algorithmic_bytes_per_launch": work["cache_bytes"],
             "mfma_TFLOPs": work["attn_flops"] / attn_s / 1e12,
             "mfma_frac": work["attn_flops"] / attn_s / 1e12 / MFMA_PEAK_TFLOPS,

@@ -151,17 +151,26 @@ __device__ __forceinline__ f32x16 score_tile(const char* cur, const int (&s_off)
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
-  // ---- which split / which half of the heads
+  // ---- which split / which half of the heads. Workgroups are dealt to the 8
+  // XCDs round-robin by id (XCD = id % 8); XCD x takes the contiguous run of
+  // work items [x n, x n + n), n = ceil(n_work / 8), so the splits of one
+  // sequence share one L2 and its queries are fetched into it once. The grid
+  // has at least n seats per XCD (2 n for Sq = 2); spare seats exit. With
+  // Sq = 2 the two head halves of a split are ids 8 apart: same XCD,
+  // dispatched together.
+  const int n_work = p.meta[0];
+  const int xcd = blockIdx.x & 7, seat = blockIdx.x >> 3;
+  const int per_xcd = (n_work + 7) >> 3;
   int k, grp;
   if (p.q_tokens == 1) {
-    k = blockIdx.x;
+    if (seat >= per_xcd) return;
+    k = xcd * per_xcd + seat;
     grp = 0;
   } else {
-    // pairs (k, 0), (k, 1) land 8 ids apart: same XCD, dispatched together
-    k = 8 * (blockIdx.x >> 4) + (blockIdx.x & 7);
-    grp = (blockIdx.x >> 3) & 1;
+    if ((seat >> 1) >= per_xcd) return;
+    k = xcd * per_xcd + (seat >> 1);
+    grp = seat & 1;
   }
-  const int n_work = p.meta[0];
   if (k >= n_work) return;
   const WorkItem wi = p.work[k];
   if (wi.slot < 0 || wi.slot >= p.max_chunks || wi.t_end <= wi.t_begin) return;
@@ -482,12 +491,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  int grid;
-  if (a.q_tokens == 1) {
-    grid = a.max_chunks;
-  } else {
-    grid = 2 * ((a.max_chunks + 7) / 8) * 8;
-  }
+  // a multiple of 8 work items per XCD row (see the mapping in the kernel)
+  const int per = (a.max_chunks + 7) / 8 * 8;
+  const int grid = a.q_tokens == 1 ? per : 2 * per;
   hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
