@@ -23,8 +23,8 @@
 //   the A operand (lane = token, 8 consecutive latent values per k-step, one
 //   16-byte LDS read), the wavefront's queries are the B operand and stay in
 //   VGPRs for the whole split (32 fp16 k-steps of the latent part, 4 bf16
-//   k-steps of the RoPE part). The chain accumulates in VGPRs (inline MFMAs,
-//   the result-to-VALU distance covered by s_nop) so O owns all 256 AGPRs.
+//   k-steps of the RoPE part). The chain accumulates in VGPRs (inline MFMAs)
+//   so O owns all 256 AGPRs.
 // * softmax: each lane owns one row (lane % 32) and 16 of the tile's 32
 //   tokens, so row max and row sum are 16 in-lane steps plus one exchange with
 //   lane ^ 32. The running max is moved only when it grows by more than 2^15
@@ -36,42 +36,43 @@
 //   half the bytes per cycle of a 16-byte read, so each wavefront reads only
 //   its quarter of the columns), the B operand (P) from LDS. O lives in 16
 //   accumulator tiles (4 column tiles x 4 row tiles, 256 registers per lane).
-// * cache tiles: 32 tokens x 1152 B = 36 KB, contiguous inside one 64-token
-//   block, in a ring of three LDS buffers. Tiles are fetched two ahead with
-//   direct-to-LDS loads (global_load_lds_dwordx4: no VGPRs in flight), issued
-//   under the latent MFMAs; once a tile has landed each lane converts the
-//   c_KV granules it fetched from bf16 to fp16 in place (exact in fp16's
-//   range) and zeroes rows past the split, so NaN padding never reaches the
-//   latent MFMAs (masked scores become -inf with a select). The granule
-//   swizzle g ^ (row % 8) keeps the score reads, the transposed reads and the
-//   conversion pass free of bank conflicts; the fetch addresses apply the
+// * cache tiles: 32 tokens, contiguous inside one 64-token block. The c_KV
+//   part (32 KB) goes to a ring of four LDS buffers, the k_R part (4 KB) to a
+//   ring of three, with direct-to-LDS loads (global_load_lds_dwordx4: no VGPRs
+//   in flight). Each lane converts the c_KV granules it fetched from bf16 to
+//   fp16 in place (exact in fp16's range) and zeroes rows past the split, so
+//   NaN padding never reaches the latent MFMAs (masked scores become -inf
+//   with a select). Granules are stored at g ^ sw(row % 8) (a permutation of
+//   the low 3 bits), which keeps the score reads, the transposed reads and
+//   the conversion free of bank conflicts; the fetch addresses apply the
 //   inverse permutation.
-// * per tile, one barrier: scores, softmax, P to LDS, conversion of the next
-//   tile | barrier | rescale (rare), latent accumulation, fetch of the tile
-//   after next.
+// * software pipeline, one barrier per tile. Iteration i issues, in one
+//   stream, the latent MFMAs of tile i, the score MFMAs of tile i + 1, the
+//   conversion of tile i + 2 and the fetch of tile i + 3; the softmax of tile
+//   i + 1 runs on the VALU under the second half of tile i's latent MFMAs. The
+//   barrier then publishes P and the converted tile for the next iteration.
 #include "common.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kGranPerRow = kRowBytes / 16;               // 72
-constexpr int kTileBytes = kTileTok * kRowBytes;          // 36864
 constexpr int kThreads = kWaves * 64;                     // 256
-constexpr int kFetch = kTileBytes / 16 / kThreads;        // 9 granules per lane per tile
-constexpr int kNBuf = 3;                                  // LDS tile ring
+constexpr int kKvBytes = kTileTok * kDLat * 2;            // 32 KB: c_KV of a tile, 1 KB rows
+constexpr int kKrBytes = kTileTok * kDRope * 2;           // 4 KB: k_R of a tile, 128 B rows
+constexpr int kNKv = 4;                                   // c_KV ring: tiles i .. i + 3
+constexpr int kNKr = 3;                                   // k_R ring: tiles i + 1 .. i + 3
 constexpr int kColsPerWave = kDLat / kWaves;              // 128
-constexpr int kQpWaveBytes = kRowsPerWave * kDRope * 2;   // 4 KB of q_pe per wavefront
 constexpr int kPBytes = kRowsPerWg * kTileTok * 2;        // 8 KB of P per tile
 // LDS map
-constexpr int kOffQp = kNBuf * kTileBytes;                       // 110592
-constexpr int kOffP = kOffQp + kWaves * kQpWaveBytes;            // 126976: P, 2 parities
-constexpr int kOffAlpha = kOffP + 2 * kPBytes;                   // 143360: rescale, 2 parities
-constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWg * 4;         // 144384: per-wave flags
-constexpr int kOffStat = kOffFlag + 2 * kWaves * 4;              // 144416: 1/l per row
-constexpr int kLdsBytes = kOffStat + kRowsPerWg * 4;             // 144928
+constexpr int kOffKr = kNKv * kKvBytes;                          // 131072
+constexpr int kOffP = kOffKr + kNKr * kKrBytes;                  // 143360: P, 2 parities
+constexpr int kOffAlpha = kOffP + 2 * kPBytes;                   // 159744: rescale, 2 parities
+constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWg * 4;         // 160768: per-wave flags
+constexpr int kLdsBytes = kOffFlag + 2 * kWaves * 4;             // 160800
 constexpr int kEpiBytes = kWaves * kRowsPerWg * kColsPerWave * 2;   // 131072 transpose space
-static_assert(kEpiBytes <= kOffAlpha, "epilogue space must not reach the statistics");
+constexpr int kOffStat = kOffKr;                                 // 1/l per row, after the loop
+static_assert(kEpiBytes <= kOffKr, "epilogue space is the c_KV ring");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 constexpr float kRescaleLog2 = 15.0f;   // lazy max threshold: p = 2^(x - m) < 2^15
 
@@ -116,37 +117,13 @@ __device__ __forceinline__ f16x8 lds_read_tr(const char* p0, const char* p1) {
   return __builtin_bit_cast(f16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Scores of one tile for this wavefront's 32 rows: D[token, row] over 32 fp16
-// k-steps (latent) and 4 bf16 k-steps (RoPE), accumulated in VGPRs; dependent
-// MFMAs on one accumulator issue back to back, s_nop 15 covers the
-// MFMA-result -> VALU-read distance. A fragments are read 4 MFMAs ahead.
-__device__ __forceinline__ f32x16 score_tile(const char* cur, const int (&s_off)[4],
-                                             const f16x8 (&qa)[32], const char* qp_row,
-                                             int qp_x) {
-  constexpr int kPre = 4;
-  f16x8 a[kPre];
-#pragma unroll
-  for (int j = 0; j < kPre; ++j) a[j] = lds_read16<f16x8>(cur, s_off[j & 3] + 128 * (j >> 2));
-  f32x16 s;
-  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=v"(s) : "v"(a[0]), "v"(qa[0]));
-  a[0] = lds_read16<f16x8>(cur, s_off[0] + 128);
-#pragma unroll
-  for (int ks = 1; ks < 32; ++ks) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
-                 : "+v"(s)
-                 : "v"(a[ks % kPre]), "v"(qa[ks]));
-    const int nk = ks + kPre;
-    if (nk < 32) a[ks % kPre] = lds_read16<f16x8>(cur, s_off[nk & 3] + 128 * (nk >> 2));
-  }
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 ar = lds_read16<bf16x8>(cur, s_off[ks] + 128 * 8);
-    const bf16x8 br = lds_read16<bf16x8>(qp_row, 16 * ((2 * ks + (qp_x >> 3)) ^ (qp_x & 7)));
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ar), "v"(br));
-  }
-  asm volatile("s_nop 15" : "+v"(s));
-  return s;
-}
+// score-chain MFMAs: accumulator in VGPRs, issued in program order
+#define S_MFMA_FIRST(acc, a, b) \
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b))
+#define S_MFMA(acc, a, b) \
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
+#define S_MFMA_BF16(acc, a, b) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
 
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -191,15 +168,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   const int lim = min(wi.t_end, n_vis);                       // tokens this wave may use
   const int rr = 32 * w + l32;                                // this lane's score row
 
-  // ---- fetch plan: wave w, fetch j moves LDS granule slots P = 256 j + 64 w +
-  // lane; slot P holds logical granule (P % 72) ^ (row % 8) of row P / 72
-  // (P / 72 == (P * 3641) >> 18 for P < 2304). Offsets are recomputed per use.
-  int t_f = t;   // re-materialised each tile so the offsets are not hoisted
-  auto slot_row = [&](int j) { return ((kThreads * j + t_f) * 3641) >> 18; };
-  auto fetch_off = [&](int j) -> unsigned {
-    const int P = kThreads * j + t_f, row = slot_row(j);
-    return row * kRowBytes + 16 * ((P - row * kGranPerRow) ^ (row & 7));
-  };
+  // ---- tile buffers
+  auto kvb = [&](int i) -> char* { return smem + (i & (kNKv - 1)) * kKvBytes; };
+  auto krb = [&](int i) -> char* { return smem + kOffKr + (i % kNKr) * kKrBytes; };
+
+  // ---- fetch plan. c_KV rows are 1 KB; logical granule g of row r is stored
+  // at g ^ sw(r % 8), sw(x) = 3-bit rotate left of x. Fetch j (0..7) of wave w
+  // moves row 4 j + w: LDS slot `lane` of it holds logical granule
+  // lane ^ sw(r % 8), and sw(r % 8) is 2 w + (j % 2). The k_R fetch moves rows
+  // 8 w .. 8 w + 7 (128 B rows, swizzle g ^ (r % 8)): lane holds row
+  // 8 w + lane / 8, slot lane % 8, logical granule (lane % 8) ^ (lane / 8).
+  const unsigned voff_even = 16u * (unsigned)(lane ^ (2 * w));
+  const unsigned voff_odd = 16u * (unsigned)(lane ^ (2 * w + 1));
+  const unsigned voff_kr =
+      (unsigned)((lane >> 3) * kRowBytes + kDLat * 2 + 16 * ((lane & 7) ^ (lane >> 3)));
   // block ids of this split, 64 per window: lane i holds the id of block
   // blk_base + i; a tile reads its id with one lane read
   const int32_t* btab = p.block_table + (size_t)b * p.max_blocks_per_seq;
@@ -208,7 +190,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   int blk_base = blk_first;
   int blk_lane = blk_first + lane <= blk_last ? btab[blk_first + lane] : 0;
   asm volatile("" : "+v"(blk_lane));   // consume the load here: later waits stay local
-  auto buf = [&](int i) -> char* { return smem + (i % kNBuf) * kTileBytes; };
   auto tile_src = [&](int ts) -> const char* {
     const int bi = ts / kBlock;
     if (bi >= blk_base + 64) {   // next window (splits longer than 4096 tokens)
@@ -220,71 +201,87 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);   // memory safety
     return (const char*)p.cache + ((size_t)blk * kBlock + (ts % kBlock)) * kRowBytes;
   };
-  auto fetch_one = [&](const char* src, char* dst, int j) {
-    dma16(dst + 1024 * (4 * j + w), src, fetch_off(j));
+  auto fetch_kv = [&](const char* src, int i, int j) {
+    dma16(kvb(i) + 1024 * (4 * j + w), src + (4 * j + w) * kRowBytes,
+          (j & 1) ? voff_odd : voff_even);
   };
-  // in-place bf16 -> fp16 of the c_KV granules this lane fetched; rows past the
-  // split become zeros. Reads first, then conversions and writes.
-  auto convert_tile = [&](char* tb, int ts) {
-    const int valid = wi.t_end - ts;
-    u32x4 v[kFetch];
-#pragma unroll
-    for (int j = 0; j < kFetch; ++j) {
-      const int row = slot_row(j);
-      if (kThreads * j + t_f - row * kGranPerRow < kDLat / 8)
-        v[j] = *(const u32x4*)(tb + 16 * (kThreads * j + t_f));
-    }
-#pragma unroll
-    for (int j = 0; j < kFetch; ++j) {
-      const int row = slot_row(j);
-      if (kThreads * j + t_f - row * kGranPerRow < kDLat / 8)
-        *(u32x4*)(tb + 16 * (kThreads * j + t_f)) =
-            row < valid ? bf16x8_to_f16x8(v[j]) : u32x4{0, 0, 0, 0};
-    }
+  auto fetch_kr = [&](const char* src, int i) {
+    dma16(krb(i) + 1024 * w, src + 8 * w * kRowBytes, voff_kr);
+  };
+  // in-place bf16 -> fp16 of c_KV granule j this lane fetched (row 4 j + w);
+  // rows at or past `valid` become zeros
+  auto convert_one = [&](char* tb, int j, int valid) {
+    u32x4* q = (u32x4*)(tb + 1024 * (4 * j + w) + 16 * lane);
+    const u32x4 v = *q;
+    unsigned keep = (4 * j + w) < valid ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(keep));
+    const u32x4 c = bf16x8_to_f16x8(v);
+    *q = u32x4{c[0] & keep, c[1] & keep, c[2] & keep, c[3] & keep};
   };
 
-  // ---- queries: latent part -> VGPRs (B operands: lane = row, 8 consecutive
-  // k), RoPE part -> this wave's LDS slice (rows, granule ^ row % 8)
+  // ---- prologue fetch of tile 0 (tiles 1 and 2 follow once the queries are in)
+  const int n_tiles = (wi.t_end - wi.t_begin + kTileTok - 1) / kTileTok;
+  const int t0 = wi.t_begin;
+  auto fetch_tile = [&](int i) {
+    const char* src = tile_src(t0 + i * kTileTok);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fetch_kv(src, i, j);
+    fetch_kr(src, i);
+  };
+  fetch_tile(0);
+
+  // ---- queries: latent part and RoPE part -> VGPRs (B operands: lane = row,
+  // 8 consecutive k)
   f16x8 qa[32];
+  bf16x8 qp[4];
   {
     const u32x4* src = (const u32x4*)(p.q_abs + ((size_t)(r * 4 + hg) * 32) * 64 * 8);
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) qa[ks] = __builtin_bit_cast(f16x8, src[ks * 64 + lane]);
-    // wait for them here: a wait inside the loop would also drain the fetches
+    const uint16_t* qsrc = p.q_pe + ((size_t)r * kHeads + hg * 32 + l32) * kDRope + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qp[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qsrc + 16 * ks));
+    // the compiler waits for these (and so for tile 0) here: a wait inside
+    // the loop would also drain the fetches
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qa[ks]));
-  }
-  char* qp_lds = smem + kOffQp + w * kQpWaveBytes;
-  {
-    const uint16_t* src = p.q_pe + ((size_t)r * kHeads + hg * 32) * kDRope;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int G = lane + 64 * n, row = G >> 3, g = G & 7;
-      *(u32x4*)(qp_lds + row * 128 + 16 * (g ^ (row & 7))) = *(const u32x4*)(src + 8 * G);
-    }
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qp[ks]));
   }
-  const char* qp_row = qp_lds + l32 * 128;
-  const int qp_x = 8 * half + (l32 & 7);   // k-half of the B fragment, row swizzle
+  MLA_WAIT_VM(0);
+  // tiles 1 and 2 land under the conversion, scores and softmax of tile 0
+  for (int i = 1; i < 3 && i < n_tiles; ++i) fetch_tile(i);
 
   // ---- per-lane LDS offsets
-  // scores: row = l32, logical granule 2 ks + half (+64 for k_R)
-  int s_off[4];
+  // c_KV swizzle: sw(x) = ((x & 3) << 1) | (x >> 2) for x < 8, a permutation,
+  // so 8 consecutive rows put one logical granule in 8 different bank groups
+  // (score reads), and rows 4 k .. 4 k + 3 put the granule pair {2 m, 2 m + 1}
+  // in 8 different ones (transposed reads); rows are 1 KB apart, so every row
+  // starts in the same bank.
+  auto sw = [](int x) { return ((x & 3) << 1) | (x >> 2); };
+  // scores: row = l32, logical granule 2 ks + half; k-step ks reads
+  // s_off[ks % 4] + 128 (ks / 4) (the swizzle only moves the low 3 bits); k_R
+  // k-step ks reads r_off[ks] in the k_R buffer
+  int s_off[4], r_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s_off[j] = l32 * kRowBytes + 16 * ((2 * j + half) ^ (l32 & 7));
+  for (int j = 0; j < 4; ++j) {
+    s_off[j] = l32 * 1024 + 16 * ((2 * j + half) ^ sw(l32 & 7));
+    r_off[j] = l32 * 128 + 16 * ((2 * j + half) ^ (l32 & 7));
+  }
   // transposed reads of this wave's columns. MFMA k-slot (hh, e) of k-step st
   // is token 16 st + 8 (e / 4) + 4 hh + e % 4 (the score accumulator's token
   // order). Group gg = lane / 16 (k-half hh = gg / 2, 16-column half gg % 2);
   // for read q source lane L addresses token 16 st + 8 q + 4 hh + L / 4 at
-  // column 128 w + 32 ct + 16 (gg % 2) + 4 (L % 4). The row swizzle (row % 8)
-  // is the same for every st and q, so one base per column tile serves them
-  // all (st and q add immediates).
+  // column 128 w + 32 ct + 16 (gg % 2) + 4 (L % 4). The row swizzle
+  // (sw(row % 8)) is the same for every st and q, so one base per column tile
+  // serves them all (st and q add immediates).
   const int gg = lane >> 4, Lq = lane & 15, hh = gg >> 1;
   int tr_off[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const int row = 4 * hh + (Lq >> 2);
     const int col = kColsPerWave * w + 32 * ct + 16 * (gg & 1) + 4 * (Lq & 3);
-    tr_off[ct] = row * kRowBytes + 16 * ((col >> 3) ^ (row & 7)) + 2 * (col & 7);
+    tr_off[ct] = row * 1024 + 16 * ((col >> 3) ^ sw(row & 7)) + 2 * (col & 7);
   }
   // P: [row][32 positions] fp16, 64 B per row, 16-byte chunk c stored at
   // c ^ ((row / 2) % 4). Position 16 st + 8 hh + e holds the token of k-slot
@@ -299,44 +296,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   float m = -INFINITY, l = 0.f;   // statistics of this lane's score row
   const float scale_log2 = p.scale_log2;
 
-  // ---- prologue: tile 0 converted, tile 1 in flight
-  const int n_tiles = (wi.t_end - wi.t_begin + kTileTok - 1) / kTileTok;
-  const int t0 = wi.t_begin;
-  {
-    const char* src = tile_src(t0);
+  // softmax of one tile's scores (tile start ts, parity par): P and the rescale
+  // factor to LDS, the running statistics updated. Straight-line code, so it
+  // can be interleaved with independent MFMAs.
+  auto softmax_tile = [&](f32x16 s, int ts, int par) {
+    // s[i] is token ts + 8 (i / 4) + 4 half + i % 4
+    const int nv = lim - ts - 4 * half;   // tokens of this lane's k-half below lim
 #pragma unroll
-    for (int j = 0; j < kFetch; ++j) fetch_one(src, buf(0), j);
-    if (n_tiles > 1) {
-      src = tile_src(t0 + kTileTok);
-#pragma unroll
-      for (int j = 0; j < kFetch; ++j) fetch_one(src, buf(1), j);
-      MLA_WAIT_VM(9);
-    } else {
-      MLA_WAIT_VM(0);
-    }
-  }
-  convert_tile(buf(0), t0);
-  MLA_WAIT_LGKM0();
-  MLA_BARRIER();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    asm volatile("" : "+v"(t_f));
-    const int ts = t0 + it * kTileTok;
-    const int par = it & 1;
-    const char* cur = buf(it);
-    char* pbuf = smem + kOffP + par * kPBytes;
-
-    // -- scores and softmax of this wave's rows
-    f32x16 s = score_tile(cur, s_off, qa, qp_row, qp_x);
-    // s[i] is token 8 (i/4) + 4 half + i%4; masking only on a split's last
-    // tile or a query's last visible one
-    if (ts + kTileTok > lim) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = ts + 8 * (i >> 2) + 4 * half + (i & 3);
-        s[i] = tok < lim ? s[i] : -INFINITY;
-      }
-    }
+    for (int i = 0; i < 16; ++i) s[i] = (8 * (i >> 2) + (i & 3)) < nv ? s[i] : -INFINITY;
     float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                      fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
@@ -347,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     // O rows hold earlier tiles relative to m; they scale by 2^(m - m_new)
     const bool rescale = grow && m != -INFINITY;
     const float alpha = rescale ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-    const unsigned long long any_rescale = __ballot(rescale);
+    const int any_rescale = __ballot(rescale) != 0ull;
     m = m_new;
     const float neg_m = (m == -INFINITY) ? 0.f : -m;
     float rs = 0.f;
@@ -360,87 +327,220 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     }
     rs += __shfl_xor(rs, 32);
     l = l * alpha + rs;
-    // P rows to LDS: registers 4 q .. 4 q + 3 are tokens 8 q + 4 half + 0..3,
-    // i.e. k-step q / 2, k-half `half`, slots 4 (q % 2) .. + 3: chunk
-    // 2 (q / 2) + half, 8 bytes in at 8 (q % 2)
+    // registers 4 q .. 4 q + 3 are tokens 8 q + 4 half + 0..3, i.e. k-step
+    // q / 2, k-half `half`, slots 4 (q % 2) .. + 3: chunk 2 (q / 2) + half,
+    // 8 bytes in at 8 (q % 2)
+    char* pbuf = smem + kOffP + par * kPBytes;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *(f16x4*)(pbuf + p_chunk(rr, 2 * (q >> 1) + half) + 8 * (q & 1)) = pq[q];
-    if (any_rescale) {
-      if (half == 0) ((float*)(smem + kOffAlpha + par * kRowsPerWg * 4))[rr] = alpha;
-    }
-    if (lane == 0) ((int*)(smem + kOffFlag + par * kWaves * 4))[w] = any_rescale ? 1 : 0;
+    // both half-waves store the same values (no divergent branch)
+    ((float*)(smem + kOffAlpha + par * kRowsPerWg * 4))[rr] = alpha;
+    ((int*)(smem + kOffFlag + par * kWaves * 4))[w] = any_rescale;
+  };
 
-    // -- the next tile has landed (its fetch was issued one tile ago): convert
-    if (it + 1 < n_tiles) {
-      MLA_WAIT_VM(0);
-      convert_tile(buf(it + 1), ts + kTileTok);
-    }
-    MLA_WAIT_LGKM0();
-    MLA_BARRIER();
-
-    // -- rescale O rows whose reference moved (rare)
-    {
-      const int4 fl = *(const int4*)(smem + kOffFlag + par * kWaves * 4);
-      if (fl.x | fl.y | fl.z | fl.w) {
-        const float* al = (const float*)(smem + kOffAlpha + par * kRowsPerWg * 4);
-        float ah[4];
+  // rescale O rows whose reference moved (rare); flags / factors of parity par
+  auto rescale_o = [&](int par) {
+    const int4 fl = *(const int4*)(smem + kOffFlag + par * kWaves * 4);
+    if (fl.x | fl.y | fl.z | fl.w) {
+      const float* al = (const float*)(smem + kOffAlpha + par * kRowsPerWg * 4);
+      float ah[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int4 f4 = fl;
-          const int fh = h == 0 ? f4.x : h == 1 ? f4.y : h == 2 ? f4.z : f4.w;
-          ah[h] = fh ? al[32 * h + l32] : 1.f;
-        }
-        // O *= alpha in place in the accumulator registers (read / multiply /
-        // write per element, so O never leaves the AGPRs); the s_nops cover
-        // the MFMA -> accumulator-read and write -> MFMA distances.
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float x = o[c][h][i], tmp;
-              asm volatile(
-                  "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                  : "+a"(x), "=&v"(tmp)
-                  : "v"(ah[h]));
-              o[c][h][i] = x;
-            }
-        asm volatile("s_nop 7" ::: "memory");
+      for (int h = 0; h < 4; ++h) {
+        const int fh = h == 0 ? fl.x : h == 1 ? fl.y : h == 2 ? fl.z : fl.w;
+        ah[h] = fh ? al[32 * h + l32] : 1.f;
       }
-    }
-
-    // -- latent accumulation of this wave's 128 columns, all 128 rows; the
-    // fetch of the tile after next (into the buffer tile it - 1 used) is
-    // issued under the MFMAs
-    const bool far = it + 2 < n_tiles;
-    const char* fsrc = far ? tile_src(ts + 2 * kTileTok) : nullptr;
-    char* fdst = buf(it + 2);
+      // O *= alpha in place in the accumulator registers (read / multiply /
+      // write per element, so O never leaves the AGPRs); the s_nops cover
+      // the MFMA -> accumulator-read and write -> MFMA distances.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f16x8 pb[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        pb[h] = lds_read16<f16x8>(pbuf, p_chunk(32 * h + l32, 2 * st + half));
-      f16x8 a_next = lds_read_tr(cur + tr_off[0] + 16 * kRowBytes * st,
-                                 cur + tr_off[0] + 16 * kRowBytes * st + 8 * kRowBytes);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const f16x8 a = a_next;
-        if (ct + 1 < 4)
-          a_next = lds_read_tr(cur + tr_off[ct + 1] + 16 * kRowBytes * st,
-                               cur + tr_off[ct + 1] + 16 * kRowBytes * st + 8 * kRowBytes);
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          o[ct][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[h], o[ct][h], 0, 0, 0);
-        const int j = 4 * st + ct;   // 8 of the 9 fetches here, the last after the loop
-        if (far) fetch_one(fsrc, fdst, j);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = o[c][h][i], tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(ah[h]));
+            o[c][h][i] = x;
+          }
+      asm volatile("s_nop 7" ::: "memory");
+    }
+  };
+
+  // latent MFMAs of one k-step (16 tokens) of tile `cur` with P of parity par
+  auto pv_step = [&](const char* cur, const char* pbuf, int st) {
+    f16x8 pb[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pb[h] = lds_read16<f16x8>(pbuf, p_chunk(32 * h + l32, 2 * st + half));
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f16x8 a = lds_read_tr(cur + tr_off[ct] + 1024 * 16 * st,
+                                  cur + tr_off[ct] + 1024 * (16 * st + 8));
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o[ct][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[h], o[ct][h], 0, 0, 0);
+    }
+  };
+
+  // ---- prologue: convert tile 0; scores and softmax of tile 0; convert tile 1
+#pragma unroll
+  for (int j = 0; j < 8; ++j) convert_one(kvb(0), j, wi.t_end - t0);
+  MLA_WAIT_LGKM0();
+  MLA_BARRIER();
+  {
+    const char* kv = kvb(0);
+    const char* kr = krb(0);
+    f32x16 s;
+    f16x8 sa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sa[j] = lds_read16<f16x8>(kv, s_off[j]);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      if (ks == 0) {
+        S_MFMA_FIRST(s, sa[0], qa[0]);
+      } else {
+        S_MFMA(s, sa[ks & 3], qa[ks]);
+      }
+      const int nk = ks + 4;
+      if (nk < 32) sa[ks & 3] = lds_read16<f16x8>(kv, s_off[nk & 3] + 128 * (nk >> 2));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = lds_read16<bf16x8>(kr, r_off[ks]);
+      S_MFMA_BF16(s, a, qp[ks]);
+    }
+    asm volatile("s_nop 15" : "+v"(s));
+    softmax_tile(s, t0, 0);
+  }
+  if (n_tiles > 1) {
+    // tile 1 has landed once at most tile 2's 9 fetches are outstanding
+    if (n_tiles > 2) {
+      MLA_WAIT_VM(9);
+    } else {
+      MLA_WAIT_VM(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) convert_one(kvb(1), j, wi.t_end - t0 - kTileTok);
+  }
+  MLA_WAIT_LGKM0();
+  MLA_BARRIER();
+
+  // ---- main loop: iteration i = latent pass of tile i, scores and softmax of
+  // tile i + 1, conversion of tile i + 2, fetch of tile i + 3. The body is the
+  // same straight-line MFMA stream for every i: near the end of the split the
+  // fetch re-reads the last tile (an L2 hit) into the free buffer of tile
+  // i + 3 and the conversion works on the dead buffer of tile i + 2, so no
+  // branch splits the stream; all fetches are drained before the epilogue.
+  const int t_last = t0 + (n_tiles - 1) * kTileTok;
+  auto iteration = [&](int i) {
+    const int ts = t0 + i * kTileTok;
+    const char* cur = kvb(i);
+    const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
+    const char* kv1 = kvb(i + 1);
+    const char* kr1 = krb(i + 1);
+    const char* fsrc = tile_src(min(ts + 3 * kTileTok, t_last));
+    char* cbuf = kvb(i + 2);
+    const int cvalid = wi.t_end - (ts + 2 * kTileTok);
+
+    rescale_o(i & 1);
+
+    // phase 1: score chain of tile i + 1 (32 fp16 + 4 bf16 MFMAs, operands
+    // read 4 k-steps ahead) with 8 latent MFMAs of tile i (k-step 0, column
+    // tiles 0 and 1). Conversion of tile i + 2 on a 4-MFMA cadence: group j
+    // converts granule j - 1 two dwords per MFMA (3 MFMAs after its read),
+    // writes it, then waits for fetch j of tile i + 2, reads granule j and
+    // issues fetch j of tile i + 3 (the k_R fetch in group 8).
+    f16x8 pb[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pb[h] = lds_read16<f16x8>(pbuf, p_chunk(32 * h + l32, half));
+    f16x8 ta = lds_read_tr(cur + tr_off[0], cur + tr_off[0] + 1024 * 8);
+    auto s_frag = [&](int ks) -> f16x8 {
+      return ks < 32 ? lds_read16<f16x8>(kv1, s_off[ks & 3] + 128 * (ks >> 2))
+                     : lds_read16<f16x8>(kr1, r_off[ks - 32]);
+    };
+    f16x8 sa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sa[j] = s_frag(j);
+    f16x8 ta3;
+    u32x4 cv = {0, 0, 0, 0}, co;
+    unsigned keep = 0;
+    f32x16 s;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+      if (ks == 0) {
+        S_MFMA_FIRST(s, sa[0], qa[0]);
+      } else if (ks < 32) {
+        S_MFMA(s, sa[ks & 3], qa[ks]);
+      } else {
+        S_MFMA_BF16(s, __builtin_bit_cast(bf16x8, sa[ks & 3]), qp[ks - 32]);
+      }
+      const int nk = ks + 4;
+      if (nk < 36) sa[ks & 3] = s_frag(nk);
+      if ((ks & 1) && ks < 16) {
+        const int u = ks >> 1, ct = u >> 2, h = u & 3;
+        o[ct][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta, pb[h], o[ct][h], 0, 0, 0);
+        if (u == 3) ta = lds_read_tr(cur + tr_off[1], cur + tr_off[1] + 1024 * 8);
+      }
+      if (ks == 32) ta = lds_read_tr(cur + tr_off[2], cur + tr_off[2] + 1024 * 8);
+      if (ks == 34) ta3 = lds_read_tr(cur + tr_off[3], cur + tr_off[3] + 1024 * 8);
+      const int j = ks >> 2, q = ks & 3;
+      if (j >= 1 && q >= 2) {   // convert dwords 2 (q - 2), +1 of granule j - 1
+#pragma unroll
+        for (int d = 2 * (q - 2); d < 2 * (q - 2) + 2; ++d) {
+          const float lo = __builtin_bit_cast(float, cv[d] << 16);
+          const float hi = __builtin_bit_cast(float, cv[d] & 0xffff0000u);
+          co[d] = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_pkrtz(lo, hi)) & keep;
+        }
+      }
+      if (q == 3) {
+        if (j >= 1) *(u32x4*)(cbuf + 1024 * (4 * (j - 1) + w) + 16 * lane) = co;
+        MLA_WAIT_VM(8);   // this lane's fetch j of tile i + 2 has landed
+        if (j < 8) {
+          cv = *(const u32x4*)(cbuf + 1024 * (4 * j + w) + 16 * lane);
+          keep = (4 * j + w) < cvalid ? 0xffffffffu : 0u;
+          asm volatile("" : "+v"(keep));
+          fetch_kv(fsrc, i + 3, j);
+        } else {
+          fetch_kr(fsrc, i + 3);
+        }
       }
     }
-    if (far) fetch_one(fsrc, fdst, 8);
+    asm volatile("s_nop 15" : "+v"(s));
+
+    // phase 2: the other 24 latent MFMAs of tile i under the softmax of
+    // tile i + 1
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      o[2][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta, pb[h], o[2][h], 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      o[3][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta3, pb[h], o[3][h], 0, 0, 0);
+    pv_step(cur, pbuf, 1);
+    softmax_tile(s, ts + kTileTok, (i + 1) & 1);
+
+    MLA_WAIT_LGKM0();
+    MLA_BARRIER();
+  };
+  for (int i = 0; i + 1 < n_tiles; ++i) iteration(i);
+  // last tile: latent pass only
+  {
+    const int i = n_tiles - 1;
+    rescale_o(i & 1);
+    const char* cur = kvb(i);
+    const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
+    pv_step(cur, pbuf, 0);
+    pv_step(cur, pbuf, 1);
   }
+
+  // the epilogue reuses both rings: no fetch may still be landing, and every
+  // wave must be past its last read
+  MLA_WAIT_VM(0);
+  MLA_WAIT_LGKM0();
+  MLA_BARRIER();
   if (half == 0) ((float*)(smem + kOffStat))[rr] = l > 0.f ? 1.f / l : 0.f;
   {
     // lse = m + log2 l per score row, -inf when the row saw no position
@@ -455,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // ---- partial state: o_hat = O / l rounded to fp16, rows (qi, head) of 512
   // contiguous values; this wave writes columns [128 w, 128 w + 128) of all
   // 128 rows. The accumulator layout (lane = row, registers = columns) is
-  // turned row-major through this wave's 32 KB of LDS (the tile ring is free
+  // turned row-major through this wave's 32 KB of LDS (the c_KV ring is free
   // after the last barrier): 8-byte units of 4 columns, unit ^ 2 (row % 16).
   float inv_l[4];
 #pragma unroll
