@@ -40,9 +40,9 @@
 //   part (32 KB) goes to a ring of four LDS buffers, the k_R part (4 KB) to a
 //   ring of three, with direct-to-LDS loads (global_load_lds_dwordx4: no VGPRs
 //   in flight). Each lane converts the c_KV granules it fetched from bf16 to
-//   fp16 in place (exact in fp16's range) and zeroes rows past the split, so
-//   NaN padding never reaches the latent MFMAs (masked scores become -inf
-//   with a select). Granules are stored at g ^ sw(row % 8) (a permutation of
+//   fp16 in place (exact in fp16's range). Rows past the split re-read its
+//   last row, so NaN padding never reaches the latent MFMAs (their zero
+//   softmax weights cancel them; masked scores become -inf with a select). Granules are stored at g ^ sw(row % 8) (a permutation of
 //   the low 3 bits), which keeps the score reads, the transposed reads and
 //   the conversion free of bank conflicts; the fetch addresses apply the
 //   inverse permutation.
@@ -201,22 +201,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);   // memory safety
     return (const char*)p.cache + ((size_t)blk * kBlock + (ts % kBlock)) * kRowBytes;
   };
-  auto fetch_kv = [&](const char* src, int i, int j) {
-    dma16(kvb(i) + 1024 * (4 * j + w), src + (4 * j + w) * kRowBytes,
-          (j & 1) ? voff_odd : voff_even);
+  // c_KV fetch j of a tile with `valid` rows inside the split: rows at or past
+  // it re-read the last valid row, so they hold finite values that the zero
+  // softmax weights of their (masked) positions cancel; the choice is
+  // wave-uniform (scalar address arithmetic)
+  auto fetch_kv = [&](const char* src, int i, int j, int valid) {
+    const int srow = min(4 * j + w, valid - 1);
+    dma16(kvb(i) + 1024 * (4 * j + w), src + srow * kRowBytes, (j & 1) ? voff_odd : voff_even);
   };
   auto fetch_kr = [&](const char* src, int i) {
     dma16(krb(i) + 1024 * w, src + 8 * w * kRowBytes, voff_kr);
   };
-  // in-place bf16 -> fp16 of c_KV granule j this lane fetched (row 4 j + w);
-  // rows at or past `valid` become zeros
-  auto convert_one = [&](char* tb, int j, int valid) {
+  // in-place bf16 -> fp16 of c_KV granule j this lane fetched (row 4 j + w)
+  auto convert_one = [&](char* tb, int j) {
     u32x4* q = (u32x4*)(tb + 1024 * (4 * j + w) + 16 * lane);
-    const u32x4 v = *q;
-    unsigned keep = (4 * j + w) < valid ? 0xffffffffu : 0u;
-    asm volatile("" : "+v"(keep));
-    const u32x4 c = bf16x8_to_f16x8(v);
-    *q = u32x4{c[0] & keep, c[1] & keep, c[2] & keep, c[3] & keep};
+    *q = bf16x8_to_f16x8(*q);
   };
 
   // ---- prologue fetch of tile 0 (tiles 1 and 2 follow once the queries are in)
@@ -225,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   auto fetch_tile = [&](int i) {
     const char* src = tile_src(t0 + i * kTileTok);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fetch_kv(src, i, j);
+    for (int j = 0; j < 8; ++j) fetch_kv(src, i, j, wi.t_end - (t0 + i * kTileTok));
     fetch_kr(src, i);
   };
   fetch_tile(0);
@@ -388,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 
   // ---- prologue: convert tile 0; scores and softmax of tile 0; convert tile 1
 #pragma unroll
-  for (int j = 0; j < 8; ++j) convert_one(kvb(0), j, wi.t_end - t0);
+  for (int j = 0; j < 8; ++j) convert_one(kvb(0), j);
   MLA_WAIT_LGKM0();
   MLA_BARRIER();
   {
@@ -424,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       MLA_WAIT_VM(0);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) convert_one(kvb(1), j, wi.t_end - t0 - kTileTok);
+    for (int j = 0; j < 8; ++j) convert_one(kvb(1), j);
   }
   MLA_WAIT_LGKM0();
   MLA_BARRIER();
@@ -442,9 +441,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
     const char* kv1 = kvb(i + 1);
     const char* kr1 = krb(i + 1);
-    const char* fsrc = tile_src(min(ts + 3 * kTileTok, t_last));
+    const int fts = min(ts + 3 * kTileTok, t_last);
+    const char* fsrc = tile_src(fts);
+    const int fvalid = wi.t_end - fts;
     char* cbuf = kvb(i + 2);
-    const int cvalid = wi.t_end - (ts + 2 * kTileTok);
 
     rescale_o(i & 1);
 
@@ -467,7 +467,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     for (int j = 0; j < 4; ++j) sa[j] = s_frag(j);
     f16x8 ta3;
     u32x4 cv = {0, 0, 0, 0}, co;
-    unsigned keep = 0;
     f32x16 s;
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
@@ -493,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
         for (int d = 2 * (q - 2); d < 2 * (q - 2) + 2; ++d) {
           const float lo = __builtin_bit_cast(float, cv[d] << 16);
           const float hi = __builtin_bit_cast(float, cv[d] & 0xffff0000u);
-          co[d] = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_pkrtz(lo, hi)) & keep;
+          co[d] = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_pkrtz(lo, hi));
         }
       }
       if (q == 3) {
@@ -501,9 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
         MLA_WAIT_VM(8);   // this lane's fetch j of tile i + 2 has landed
         if (j < 8) {
           cv = *(const u32x4*)(cbuf + 1024 * (4 * j + w) + 16 * lane);
-          keep = (4 * j + w) < cvalid ? 0xffffffffu : 0u;
-          asm volatile("" : "+v"(keep));
-          fetch_kv(fsrc, i + 3, j);
+          fetch_kv(fsrc, i + 3, j, fvalid);
         } else {
           fetch_kr(fsrc, i + 3);
         }

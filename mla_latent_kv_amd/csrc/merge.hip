@@ -8,26 +8,28 @@
 // "DeepSeek-V3" page, ailearn.mscapital.top, MLA section; m.lsln.cn article,
 // section 2.2).
 //
-// One workgroup of 16 wavefronts per (head, 32 query rows), so W_UV[h] is read
-// once per 32 rows:
-//  1a. per row: M and 1 / sum 2^(lse - M) by wavefront reductions;
-//  1b. per (row, 8-column chunk) unit: the weighted sum over splits, streamed
-//      as 16-byte loads; when the workgroup has few rows, the splits of a unit
-//      are spread over up to 8 thread groups and summed afterwards in a fixed
-//      order (deterministic); o_lat goes to LDS as bf16 hi + lo pairs
-//      (hi = bf16(x), lo = bf16(x - hi), together within 2^-16 of x);
-//  2.  out = W_UV[h] o_lat on 32x32x16 bf16 MFMA (W_UV exact, hi and lo
-//      accumulated in fp32): 4 value tiles x 4 latent quarters over the 16
-//      wavefronts, quarter sums added in a fixed order.
+// One workgroup of 8 wavefronts per (head, 16 query rows). The row groups of
+// one head run on one XCD (ids 8 apart), so W_UV[h] crosses HBM once and is
+// then served by that XCD's L2.
+//  1. thread (row, 32-lane slot) sums 2 units of 8 latent values over the
+//     row's splits, 8 splits per round trip (their lse values and 16-byte
+//     partial loads together; 32 lanes read 512 contiguous bytes of a partial
+//     row), with a running max across rounds; o_lat goes to LDS as bf16 hi +
+//     lo (hi = bf16(x), lo = bf16(x - hi), together within 2^-16 of x).
+//  2. out^T[v, r] = W_UV[h][v, :] . o_lat[r, :] on 16x16x32 bf16 MFMA (W_UV
+//     exact, hi and lo accumulated in fp32): wavefront w owns value tile w
+//     (16 values); its W_UV fragments are loaded at the start and arrive while
+//     phase 1 streams the partials.
+// No atomics: every output is written once, so results are deterministic.
 #include "common.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kMThreads = 1024;
-constexpr int kMRows = 32;
-constexpr int kUnits = kMRows * (kDLat / 8);   // 2048 (row, 8-column) units
+constexpr int kMThreads = 512;
+constexpr int kMRows = 16;        // query rows per workgroup
+constexpr int kKSteps = kDLat / 32;   // 16 k-steps of 32 latent values
 
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float x) {
   unsigned int u = __builtin_bit_cast(unsigned int, x);
@@ -39,193 +41,129 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short h) {
   return __builtin_bit_cast(float, (unsigned int)h << 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
-}
-
 __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const SeqInfo* __restrict__ seqinfo,
                                                           const uint16_t* __restrict__ w_uv,
                                                           float* __restrict__ out, int rows,
-                                                          int q_tokens) {
-  __shared__ __attribute__((aligned(16))) unsigned short lat_hi[kMRows * kDLat];
-  __shared__ __attribute__((aligned(16))) unsigned short lat_lo[kMRows * kDLat];
-  __shared__ __attribute__((aligned(16))) float red[16 * 64 * 16];   // 64 KB of partial sums
-  __shared__ float row_m[kMRows], row_inv[kMRows];
-  __shared__ int row_base[kMRows], row_cnt[kMRows], row_prow[kMRows];
+                                                          int q_tokens, int groups) {
+  // o_lat of the workgroup's rows as bf16 hi / lo: [row][64 granules of 8],
+  // granule g of row r stored at g ^ r (16 rows: 16 different bank groups)
+  __shared__ __attribute__((aligned(16))) unsigned short lat[2][kMRows * kDLat];
 
-  const int h = blockIdx.x;
-  const int r0 = blockIdx.y * kMRows;
-  const int rt = min(kMRows, rows - r0);
+  // heads x, x + 8, ... run on XCD x; the row groups of a head are consecutive there
+  const int xcd = blockIdx.x & 7, seat = blockIdx.x >> 3;
+  const int h = (seat / groups) * 8 + xcd;
+  const int r0 = (seat % groups) * kMRows;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
   const size_t rpc = (size_t)q_tokens * kHeads;   // partial rows per split slot
 
-  // W_UV fragments for phase 2, issued first so they arrive during the merge:
-  // wave w covers value tile vt = w % 4 (32 values) and latent quarter kq = w / 4.
-  const int vt = w & 3, kq = w >> 2;
-  bf16x8 wa[8];
+  // W_UV fragments for phase 2 (A operand: lane = value, 8 consecutive latent
+  // values): value tile w, k-step kk
+  bf16x8 wa[kKSteps];
   {
-    const uint16_t* src = w_uv + ((size_t)h * kDV + 32 * vt + l32) * kDLat + 128 * kq + 8 * half;
+    const uint16_t* src = w_uv + ((size_t)h * kDV + 16 * w + (lane & 15)) * kDLat + 8 * (lane >> 4);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) wa[k] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 16 * k));
+    for (int kk = 0; kk < kKSteps; ++kk)
+      wa[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 32 * kk));
   }
 
-  // ---- 1a: per-row max and normaliser
-  for (int rl = w; rl < kMRows; rl += 16) {
-    float mx = -INFINITY, den = 0.f;
-    int base = 0, cnt = 0;
-    size_t prow = 0;
-    if (rl < rt) {
-      const int r = r0 + rl;
-      const SeqInfo si = seqinfo[r / q_tokens];
-      prow = (size_t)(r % q_tokens) * kHeads + h;
-      base = si.base;
-      cnt = si.count;
-      for (int s = lane; s < cnt; s += 64) mx = fmaxf(mx, part_lse[(base + s) * rpc + prow]);
-      mx = wave_max(mx);
-      if (mx != -INFINITY) {
-        for (int s = lane; s < cnt; s += 64)
-          den += __builtin_amdgcn_exp2f(part_lse[(base + s) * rpc + prow] - mx);
-        den = wave_sum(den);
-      }
-    }
-    if (lane == 0) {
-      row_m[rl] = mx == -INFINITY ? 0.f : mx;
-      row_inv[rl] = den > 0.f ? 1.f / den : 0.f;
-      row_base[rl] = base;
-      row_cnt[rl] = den > 0.f ? cnt : 0;
-      row_prow[rl] = (int)prow;
-    }
-  }
-  __syncthreads();
-
-  // ---- 1b: weighted sums over splits. g split groups of kMThreads / g threads;
-  // group sg takes splits sg, sg + g, ...
-  const int active = rt * (kDLat / 8);
-  int g = 1;
-  while (g < 8 && g * 2 * active <= kMThreads) g *= 2;
-  const int per = kMThreads / g;
-  const int sg = t / per, u0 = t % per;
-  // with g > 1 every active unit is below `per` (g * active <= kMThreads), so
-  // one pass covers them; red holds exactly g * per units
-  const int u_end = g > 1 ? per : kUnits;
-  for (int u = u0; u < u_end; u += per) {
-    const int rl = u >> 6, c = u & 63;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int cnt = row_cnt[rl];
-    if (cnt > 0) {
-      const float mr = row_m[rl], inv = row_inv[rl];
-      const size_t prow = (size_t)row_prow[rl];
-      const int base = row_base[rl];
-#pragma unroll 4
-      for (int s = sg; s < cnt; s += g) {
+  // ---- 1: weighted sum over splits; thread = (row rl, slot g32), units g32 + 32 k
+  constexpr int kChunk = 8;   // splits whose loads are in flight together
+  const int rl = t >> 5, g32 = t & 31;
+  const int r = r0 + rl;
+  float acc[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+  if (r < rows) {
+    const SeqInfo si = seqinfo[r / q_tokens];
+    const size_t prow = (size_t)(r % q_tokens) * kHeads + h;
+    const int base = si.base, cnt = si.count;
+    // chunks of kChunk splits: the lse values and the partial rows of a chunk
+    // are loaded in one round trip; a running max M rescales what earlier
+    // chunks added (the same regrouping as the online softmax)
+    float mrun = -INFINITY, den = 0.f;
+    for (int s0 = 0; s0 < cnt; s0 += kChunk) {
+      float lv[kChunk];
+      f16x8 v[kChunk][2];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const int s = min(s0 + i, cnt - 1);   // past the end: re-read, weight 0
         const size_t pr = (base + s) * rpc + prow;
-        const float ws = __builtin_amdgcn_exp2f(part_lse[pr] - mr) * inv;
-        const f16x8 v = __builtin_bit_cast(f16x8, *(const u32x4*)(part_o + pr * kDLat + 8 * c));
+        lv[i] = s0 + i < cnt ? part_lse[pr] : -INFINITY;
+        const _Float16* src = part_o + pr * kDLat + 8 * g32;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += ws * (float)v[e];
+        for (int k = 0; k < 2; ++k) v[i][k] = __builtin_bit_cast(f16x8, *(const u32x4*)(src + 256 * k));
       }
+      float cm = lv[0];
+#pragma unroll
+      for (int i = 1; i < kChunk; ++i) cm = fmaxf(cm, lv[i]);
+      const float mnew = fmaxf(mrun, cm);
+      if (mnew == -INFINITY) continue;   // nothing visible yet
+      const float sc = __builtin_amdgcn_exp2f(mrun - mnew);   // 0 when mrun = -inf
+      den *= sc;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] *= sc;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const float wi = __builtin_amdgcn_exp2f(lv[i] - mnew);   // 0 for -inf
+        den += wi;
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[k][e] += wi * (float)v[i][k][e];
+      }
+      mrun = mnew;
     }
-    if (g == 1) {
-      unsigned short hi[8], lo[8];
+    const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = f32_to_bf16_rne(acc[e]);
-        lo[e] = f32_to_bf16_rne(acc[e] - bf16_to_f32(hi[e]));
-      }
-      u32x4 vh, vl;
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vh[e] = (unsigned int)hi[2 * e] | ((unsigned int)hi[2 * e + 1] << 16);
-        vl[e] = (unsigned int)lo[2 * e] | ((unsigned int)lo[2 * e + 1] << 16);
-      }
-      const int off = rl * kDLat + 8 * (c ^ (rl & 7));
-      *(u32x4*)(lat_hi + off) = vh;
-      *(u32x4*)(lat_lo + off) = vl;
-    } else {
-      float* dstp = red + ((size_t)sg * per + u) * 8;
-      *(f32x4*)dstp = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(dstp + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    }
+      for (int e = 0; e < 8; ++e) acc[k][e] *= inv;
   }
-  if (g > 1) {
-    __syncthreads();
-    for (int u = t; u < kUnits; u += kMThreads) {
-      const int rl = u >> 6, c = u & 63;
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (u < per) {
-        for (int k = 0; k < g; ++k) {
-          const float* srcp = red + ((size_t)k * per + u) * 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += srcp[e];
-        }
-      }
-      unsigned short hi[8], lo[8];
+  for (int k = 0; k < 2; ++k) {
+    unsigned short hi[8], lo[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = f32_to_bf16_rne(acc[e]);
-        lo[e] = f32_to_bf16_rne(acc[e] - bf16_to_f32(hi[e]));
-      }
-      u32x4 vh, vl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vh[e] = (unsigned int)hi[2 * e] | ((unsigned int)hi[2 * e + 1] << 16);
-        vl[e] = (unsigned int)lo[2 * e] | ((unsigned int)lo[2 * e + 1] << 16);
-      }
-      const int off = rl * kDLat + 8 * (c ^ (rl & 7));
-      *(u32x4*)(lat_hi + off) = vh;
-      *(u32x4*)(lat_lo + off) = vl;
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = f32_to_bf16_rne(acc[k][e]);
+      lo[e] = f32_to_bf16_rne(acc[k][e] - bf16_to_f32(hi[e]));
     }
+    u32x4 vh, vl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vh[e] = (unsigned int)hi[2 * e] | ((unsigned int)hi[2 * e + 1] << 16);
+      vl[e] = (unsigned int)lo[2 * e] | ((unsigned int)lo[2 * e + 1] << 16);
+    }
+    const int g = g32 + 32 * k;
+    const int off = rl * kDLat + 8 * (g ^ rl);
+    *(u32x4*)(&lat[0][off]) = vh;
+    *(u32x4*)(&lat[1][off]) = vl;
   }
   __syncthreads();
 
-  // ---- 2: D[v, row] = sum_c W_UV[h][v][c] o_lat[row][c] over this wave's
-  // latent quarter; B fragments (lane = row, 8 consecutive c) from LDS
-  f32x16 acc = {};
+  // ---- 2: D[v, r] over 16 k-steps; B fragment: lane = row (lane % 16),
+  // 8 consecutive latent values from granule 4 kk + lane / 16
+  f32x4 d = {0, 0, 0, 0};
+  const int br = lane & 15;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int gi = (16 * kq + 2 * k + half) ^ (l32 & 7);
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, *(const u32x4*)(lat_hi + l32 * kDLat + 8 * gi));
-    const bf16x8 bl = __builtin_bit_cast(bf16x8, *(const u32x4*)(lat_lo + l32 * kDLat + 8 * gi));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[k], bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[k], bl, acc, 0, 0, 0);
+  for (int kk = 0; kk < kKSteps; ++kk) {
+    const int off = br * kDLat + 8 * ((4 * kk + (lane >> 4)) ^ br);
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lat[0][off]));
+    const bf16x8 bl = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lat[1][off]));
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bh, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bl, d, 0, 0, 0);
   }
-  {
-    float* dstp = red + ((size_t)(kq * 4 + vt) * 64 + lane) * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *(f32x4*)(dstp + 4 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-  }
-  __syncthreads();
-  if (w < 4) {
-    f32x16 sum = {};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float* srcp = red + ((size_t)(k * 4 + w) * 64 + lane) * 16;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum[e] += srcp[e];
-    }
-    const int r = r0 + l32;
-    if (l32 < rt) {
-      // sum[4 q + e] is value 32 w + 8 q + 4 half + e of row r
-      float* dst = out + ((size_t)r * kHeads + h) * kDV + 32 * w + 4 * half;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(f32x4*)(dst + 8 * q) = f32x4{sum[4 * q], sum[4 * q + 1], sum[4 * q + 2], sum[4 * q + 3]};
-    }
-  }
+  // d[e] is value 16 w + 4 (lane / 16) + e of row r0 + lane % 16
+  const int ro = r0 + br;
+  if (ro < rows)
+    *(f32x4*)(out + ((size_t)ro * kHeads + h) * kDV + 16 * w + 4 * (lane >> 4)) = d;
 }
 
 }  // namespace
@@ -234,8 +172,9 @@ hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const Seq
                         const uint16_t* w_uv, float* out, int batch, int q_tokens,
                         hipStream_t stream) {
   const int rows = batch * q_tokens;
-  hipLaunchKernelGGL(merge_kernel, dim3(kHeads, (rows + kMRows - 1) / kMRows), dim3(kMThreads), 0,
-                     stream, part_o, part_lse, seqinfo, w_uv, out, rows, q_tokens);
+  const int groups = (rows + kMRows - 1) / kMRows;
+  hipLaunchKernelGGL(merge_kernel, dim3(kHeads * groups), dim3(kMThreads), 0, stream, part_o,
+                     part_lse, seqinfo, w_uv, out, rows, q_tokens, groups);
   return hipGetLastError();
 }
 

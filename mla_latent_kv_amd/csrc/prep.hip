@@ -122,14 +122,31 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
   const int lane = t & 63;
   const int w = t >> 6;
 
-  // W_UK[h][k][cb*128 .. +128] -> LDS rows k (16-byte granules, coalesced)
+  // W_UK[h][k][cb*128 .. +128] -> LDS rows k (16-byte granules, coalesced);
+  // the first 32 query rows' B fragments are loaded in the same round trip
   const uint16_t* wsrc = w_uk + ((size_t)h * kDNope) * kDLat + cb * 128;
+  u32x4 wv[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int G = t + 256 * n;
     const int k = G >> 4, g = G & 15;
-    u32x4 v = *(const u32x4*)(wsrc + (size_t)k * kDLat + g * 8);
-    *(u32x4*)(wl + k * kWStride + g * 16) = v;
+    wv[n] = *(const u32x4*)(wsrc + (size_t)k * kDLat + g * 8);
+  }
+  const int half = lane >> 5;
+  auto load_q = [&](int r0, u32x4 (&bq)[8]) {
+    const int r = r0 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      bq[ks] = r < rows ? *(const u32x4*)(q_nope + ((size_t)r * kHeads + h) * kDNope + 16 * ks + 8 * half)
+                        : u32x4{0, 0, 0, 0};
+  };
+  u32x4 bq[8];
+  load_q(0, bq);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int G = t + 256 * n;
+    const int k = G >> 4, g = G & 15;
+    *(u32x4*)(wl + k * kWStride + g * 16) = wv[n];
   }
   __syncthreads();
 
@@ -154,18 +171,14 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
 
   const int hg = h >> 5, hj = h & 31;
   const int c0 = cb * 128 + 32 * w;           // first latent column of this wave
-  const int half = lane >> 5;
   for (int r0 = 0; r0 < rows; r0 += 32) {
     const int r = r0 + (lane & 31);
     f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 bv = {0, 0, 0, 0};
-      if (r < rows)
-        bv = *(const u32x4*)(q_nope + ((size_t)r * kHeads + h) * kDNope + 16 * ks + 8 * half);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, bv), acc,
+    for (int ks = 0; ks < 8; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, bq[ks]), acc,
                                                     0, 0, 0);
-    }
+    if (r0 + 32 < rows) load_q(r0 + 32, bq);   // next 32 rows in flight under the stores
     if (r < rows) {
       // acc[4 q + e] holds column c0 + 8 q + 4 half + e of row r
 #pragma unroll
