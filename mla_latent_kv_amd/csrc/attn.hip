@@ -129,30 +129,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   // ---- which split / which half of the heads. Workgroups are dealt to the 8
-  // XCDs round-robin by id (XCD = id % 8); XCD x takes the contiguous run of
-  // work items [x n, x n + n), n = ceil(n_work / 8), so the splits of one
-  // sequence share one L2 and its queries are fetched into it once. The grid
-  // has at least n seats per XCD (2 n for Sq = 2); spare seats exit. With
-  // Sq = 2 the two head halves of a split are ids 8 apart: same XCD,
-  // dispatched together.
-  const int n_work = p.meta[0];
-  const int xcd = blockIdx.x & 7, seat = blockIdx.x >> 3;
-  const int per_xcd = (n_work + 7) >> 3;
-  int k, grp;
+  // XCDs round-robin by id (XCD = id % 8); the plan stores the work list so
+  // that position p holds an item of XCD p % 8 and each XCD runs a contiguous
+  // run of items (consecutive splits of the same sequences share one L2 and
+  // their queries are fetched into it once). With Sq = 2 the two head halves
+  // of a split are ids 8 apart: same XCD, dispatched together.
+  int pos, grp;
   if (p.q_tokens == 1) {
-    if (seat >= per_xcd) return;
-    k = xcd * per_xcd + seat;
+    pos = blockIdx.x;
     grp = 0;
   } else {
-    if ((seat >> 1) >= per_xcd) return;
-    k = xcd * per_xcd + (seat >> 1);
-    grp = seat & 1;
+    pos = ((blockIdx.x >> 4) << 3) + (blockIdx.x & 7);
+    grp = (blockIdx.x >> 3) & 1;
   }
-  if (k >= n_work) return;
-  const WorkItem wi = p.work[k];
+  if (pos >= (p.max_chunks + 7) / 8 * 8) return;
+  const WorkItem wi = p.work[pos];
   if (wi.slot < 0 || wi.slot >= p.max_chunks || wi.t_end <= wi.t_begin) return;
   const int b = wi.b;
-  const int L = p.seqinfo[b].len;
+  const int L = wi.len;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -212,10 +206,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   auto fetch_kr = [&](const char* src, int i) {
     dma16(krb(i) + 1024 * w, src + 8 * w * kRowBytes, voff_kr);
   };
-  // in-place bf16 -> fp16 of c_KV granule j this lane fetched (row 4 j + w)
-  auto convert_one = [&](char* tb, int j) {
-    u32x4* q = (u32x4*)(tb + 1024 * (4 * j + w) + 16 * lane);
-    *q = bf16x8_to_f16x8(*q);
+  // in-place bf16 -> fp16 of the c_KV granules this lane fetched (rows 4 j + w);
+  // all reads first, then the conversions and writes
+  auto convert_tile = [&](char* tb) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *(const u32x4*)(tb + 1024 * (4 * j + w) + 16 * lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(u32x4*)(tb + 1024 * (4 * j + w) + 16 * lane) = bf16x8_to_f16x8(v[j]);
   };
 
   // ---- prologue fetch of tile 0 (tiles 1 and 2 follow once the queries are in)
@@ -386,8 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   };
 
   // ---- prologue: convert tile 0; scores and softmax of tile 0; convert tile 1
-#pragma unroll
-  for (int j = 0; j < 8; ++j) convert_one(kvb(0), j);
+  convert_tile(kvb(0));
   MLA_WAIT_LGKM0();
   MLA_BARRIER();
   {
@@ -422,8 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     } else {
       MLA_WAIT_VM(0);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) convert_one(kvb(1), j);
+    convert_tile(kvb(1));
   }
   MLA_WAIT_LGKM0();
   MLA_BARRIER();
@@ -588,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  // a multiple of 8 work items per XCD row (see the mapping in the kernel)
+  // one workgroup per work-list position (two for Sq = 2)
   const int per = (a.max_chunks + 7) / 8 * 8;
   const int grid = a.q_tokens == 1 ? per : 2 * per;
   hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(kThreads), 0, stream, a);

@@ -36,10 +36,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// One split of one sequence: tokens [t_begin, t_end) of sequence b; its
-// partial softmax state goes to slot `slot`.
+// One split of one sequence: tokens [t_begin, t_end) of sequence b (whose
+// effective length is len); its partial softmax state goes to slot `slot`.
+// slot < 0 marks an unused entry of the work list.
 struct WorkItem {
-  int b, t_begin, t_end, slot;
+  int b, t_begin, t_end, slot, len, pad0, pad1, pad2;
 };
 
 // Per-sequence split summary written by the plan kernel: partial slots
@@ -73,7 +74,8 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
   L.rows = batch * q_tokens;
   const size_t rows_per_chunk = (size_t)q_tokens * kHeads;
   size_t off = 0;
-  L.work = off;    off = align_up(off + sizeof(WorkItem) * L.max_chunks, 256);
+  // the work list is stored XCD-interleaved and padded to a multiple of 8
+  L.work = off;    off = align_up(off + sizeof(WorkItem) * ((L.max_chunks + 7) / 8 * 8), 256);
   L.seqinfo = off; off = align_up(off + sizeof(SeqInfo) * batch, 256);
   L.meta = off;    off = align_up(off + 64, 256);
   L.qabs = off;    off = align_up(off + (size_t)L.rows * kHeads * kDLat * 2, 256);

@@ -97,18 +97,32 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   int slot = (int)(exc & mask);
   int full_idx = (int)((exc >> 21) & mask);
   int tail_idx = tot_full + (int)((exc >> 42) & mask);
+  // Work item k goes to position (k % n) * 8 + k / n, n = ceil(n_work / 8):
+  // the attention workgroup with id p (dealt to XCD p % 8) reads position p,
+  // so XCD x runs items [x n, x n + n), consecutive splits of the same
+  // sequences.
+  const int n_work = min(tot_all, max_chunks);
+  const int per_xcd = (n_work + 7) / 8;
+  auto pos = [&](int kk) { return (kk % per_xcd) * 8 + kk / per_xcd; };
   for (int b = b0; b < b1; ++b) {
     const int L = min(max(seq_lens[b], 0), max_len);
     const int nb = (L + C - 1) / C;
     const int nf = L / C;
     seqinfo[b] = SeqInfo{slot, nb, L, 0};
     for (int s = 0; s < nf; ++s, ++full_idx)
-      if (full_idx < max_chunks) work[full_idx] = WorkItem{b, s * C, (s + 1) * C, slot + s};
+      if (full_idx < max_chunks) work[pos(full_idx)] = WorkItem{b, s * C, (s + 1) * C, slot + s, L, 0, 0, 0};
     if (nb > nf) {
-      if (tail_idx < max_chunks) work[tail_idx] = WorkItem{b, nf * C, L, slot + nf};
+      if (tail_idx < max_chunks) work[pos(tail_idx)] = WorkItem{b, nf * C, L, slot + nf, L, 0, 0, 0};
       ++tail_idx;
     }
     slot += nb;
+  }
+  // every other position of the list's capacity is marked unused, so no
+  // workgroup ever reads an entry left from an earlier call
+  const int cap = (max_chunks + 7) / 8 * 8;
+  for (int q = t; q < cap; q += kPrepThreads) {
+    if (q >= 8 * per_xcd || (q % 8) * per_xcd + q / 8 >= n_work)
+      work[q] = WorkItem{0, 0, 0, -1, 0, 0, 0, 0};
   }
 }
 

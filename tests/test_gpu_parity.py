@@ -123,3 +123,27 @@ def test_second_token_row_matches_shorter_single_token_run():
     mt = metrics(o2[:, 0], o1[:, 0])
     say(f"row0 vs Sq=1: {mt}")
     assert mt["max_rel"] <= 1e-3 and mt["mean_rel"] <= 2e-4
+
+
+def test_shared_workspace_after_a_larger_plan():
+    """A workspace that held a larger split plan (more work-list entries) must
+    not leak any of them into a later call with a smaller plan."""
+    import torch
+    from mla_latent_kv_amd import binding, device
+    spec = synth.Spec("reuse", 4, 1, (4096, 1000, 77, 2048))
+    batch = synth.make_batch(spec, seed=11)
+    d = device.upload(batch)
+    big = binding.MLADecoder(0, max_q_tokens=2, split_target=1000)
+    small = binding.MLADecoder(0, max_q_tokens=2, split_target=7)
+    n = max(big.workspace_size(4, 1, d["max_seq_len"]), small.workspace_size(4, 1, d["max_seq_len"]))
+    args = (d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"], d["block_table"],
+            d["seq_lens"], d["max_seq_len"])
+    say("case shared workspace: split 1000 then split 7")
+    fresh = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes everywhere
+    want = small(*args, workspace=fresh).cpu().numpy()
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    big(*args, workspace=ws)
+    got = small(*args, workspace=ws).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(want).all()
+    assert np.array_equal(got, want)
