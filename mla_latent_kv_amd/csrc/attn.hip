@@ -27,7 +27,8 @@
 //   so O owns all 256 AGPRs.
 // * softmax: each lane owns one row (lane % 32) and 16 of the tile's 32
 //   tokens, so row max and row sum are 16 in-lane steps plus one exchange with
-//   lane ^ 32. The running max is moved only when it grows by more than 2^15
+//   lane ^ 32 (v_permlane32_swap, a VALU op: no LDS round trip, no wait on
+//   the LDS queue). The running max is moved only when it grows by more than 2^15
 //   (log2 units; p stays inside fp16); otherwise the stale max is kept, which
 //   is exact because the final normalisation uses the same reference for O
 //   and l. P (fp16) and the rare rescale factors go through LDS.
@@ -106,6 +107,22 @@ __device__ __forceinline__ void dma16(const char* lds, const char* base, unsigne
                : "m0");
 }
 
+// x and x of lane l ^ 32, as the two halves of v_permlane32_swap: result 0
+// holds [a lanes 0-31 | b lanes 0-31], result 1 [a lanes 32-63 | b lanes 32-63],
+// so with a = b = x lane l sees x[l] in one and x[l ^ 32] in the other. The
+// second copy goes through an empty asm so the two operands are distinct
+// values to the optimizer.
+struct Pair32 {
+  float a, b;
+};
+__device__ __forceinline__ Pair32 pair32(float x) {
+  float y = x;
+  asm volatile("" : "+v"(y));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, y), false, false);
+  return Pair32{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read16(const char* base, int off) {
   return __builtin_bit_cast(T, *(const u32x4*)(base + off));
@@ -182,8 +199,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   const int blk_first = wi.t_begin / kBlock;
   const int blk_last = (wi.t_end - 1) / kBlock;
   int blk_base = blk_first;
+  // issued before the query loads below and consumed after them: the wait for
+  // it (the oldest load) does not wait for the queries
   int blk_lane = blk_first + lane <= blk_last ? btab[blk_first + lane] : 0;
-  asm volatile("" : "+v"(blk_lane));   // consume the load here: later waits stay local
   auto tile_src = [&](int ts) -> const char* {
     const int bi = ts / kBlock;
     if (bi >= blk_base + 64) {   // next window (splits longer than 4096 tokens)
@@ -216,6 +234,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     for (int j = 0; j < 8; ++j) *(u32x4*)(tb + 1024 * (4 * j + w) + 16 * lane) = bf16x8_to_f16x8(v[j]);
   };
 
+  // ---- queries: latent part and RoPE part -> VGPRs (B operands: lane = row,
+  // 8 consecutive k), in flight together with the block ids
+  f16x8 qa[32];
+  bf16x8 qp[4];
+  {
+    const u32x4* src = (const u32x4*)(p.q_abs + ((size_t)(r * 4 + hg) * 32) * 64 * 8);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) qa[ks] = __builtin_bit_cast(f16x8, src[ks * 64 + lane]);
+    const uint16_t* qsrc = p.q_pe + ((size_t)r * kHeads + hg * 32 + l32) * kDRope + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qp[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qsrc + 16 * ks));
+  }
+  asm volatile("" : "+v"(blk_lane));   // the block ids are in: later waits stay local
+
   // ---- prologue fetch of tile 0 (tiles 1 and 2 follow once the queries are in)
   const int n_tiles = (wi.t_end - wi.t_begin + kTileTok - 1) / kTileTok;
   const int t0 = wi.t_begin;
@@ -226,25 +258,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     fetch_kr(src, i);
   };
   fetch_tile(0);
-
-  // ---- queries: latent part and RoPE part -> VGPRs (B operands: lane = row,
-  // 8 consecutive k)
-  f16x8 qa[32];
-  bf16x8 qp[4];
-  {
-    const u32x4* src = (const u32x4*)(p.q_abs + ((size_t)(r * 4 + hg) * 32) * 64 * 8);
+  // the compiler waits for the queries (and so for tile 0) here: a wait inside
+  // the loop would also drain the fetches
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) qa[ks] = __builtin_bit_cast(f16x8, src[ks * 64 + lane]);
-    const uint16_t* qsrc = p.q_pe + ((size_t)r * kHeads + hg * 32 + l32) * kDRope + 8 * half;
+  for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qa[ks]));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qp[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qsrc + 16 * ks));
-    // the compiler waits for these (and so for tile 0) here: a wait inside
-    // the loop would also drain the fetches
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) asm volatile("" : "+v"(qa[ks]));
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qp[ks]));
-  }
+  for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qp[ks]));
   MLA_WAIT_VM(0);
   // tiles 1 and 2 land under the conversion, scores and softmax of tile 0
   for (int i = 1; i < 3 && i < n_tiles; ++i) fetch_tile(i);
@@ -305,7 +324,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
                      fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                          fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+    {
+      const Pair32 pm = pair32(mt);
+      mt = fmaxf(pm.a, pm.b) * scale_log2;
+    }
     const bool grow = mt > m + kRescaleLog2;
     const float m_new = grow ? mt : m;
     // O rows hold earlier tiles relative to m; they scale by 2^(m - m_new)
@@ -322,7 +344,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       rs += e;
       pq[i >> 2][i & 3] = (_Float16)e;
     }
-    rs += __shfl_xor(rs, 32);
+    {
+      const Pair32 ps = pair32(rs);
+      rs = ps.a + ps.b;
+    }
     l = l * alpha + rs;
     // registers 4 q .. 4 q + 3 are tokens 8 q + 4 half + 0..3, i.e. k-step
     // q / 2, k-half `half`, slots 4 (q % 2) .. + 3: chunk 2 (q / 2) + half,
