@@ -42,8 +42,8 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 # the same counter reads for a plain device copy of known size (--copy-probe).
 # The figures belong to the attention source they were taken on: when the
 # source hash differs, traffic is reported as null.
-ATTN_TRAFFIC = {"src_sha256": "aa7af4f51ee5a0e32480d31c4e262c87e6580d73af98ef919baa53c1ba92236b",
-                "fetch_kib": 76213.702, "write_kib": 32896.0,
+ATTN_TRAFFIC = {"src_sha256": "85b986fef3590bab81fe984abb669ef6b5326b254ce1f558743ab3d6ee76cf73",
+                "fetch_kib": 76215.277, "write_kib": 32896.0,
                 "fetch_scale": 1.99995, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
 
