@@ -30,7 +30,16 @@ Readings where the pages are silent or garbled (each is repeated in the design doc):
 
 * softmax scale: no page gives one; 1/sqrt(d_nope + d_rope) = 1/sqrt(192),
   the width of the per-head query/key each score is a dot product over.
-* q_pe and k_R arrive already rotated; nothing here applies RoPE.
+* the decode path takes q_pe and k_R already rotated; only the cache-append
+  producer below applies RoPE.
+* RoPE (the pages name it, for the decoupled 64-d branch, without a formula):
+  the rotary embedding's own definition, consecutive pairs (x_2i, x_2i+1)
+  turned counter-clockwise by the angle pos * base^(-2i/64), base 10000, no
+  length scaling (the pages name YaRN for 128K contexts but give no
+  parameters).
+* the appended latent is c_KV = W_DKV h exactly as the pages write it (no
+  normalisation of c_KV), and k_R = RoPE(W_KR h) at the new token's position
+  L - Sq + i.
 * with Sq new tokens per sequence (all already in the cache, counted in L),
   query i sees cached positions j <= L - Sq + i.
 * k_R is one 64-d key per token shared by every head ([P5] section 2.3).
@@ -62,6 +71,8 @@ D_ROPE = 64
 D_LATENT = 512
 D_V = 128
 ROW = D_LATENT + D_ROPE  # 576 cached elements per token ([P3]: 512 + 64)
+D_HIDDEN = 7168          # model width ([P5] section 5 configuration skeleton)
+ROPE_BASE = 10000.0      # reading: the rotary embedding's own base
 
 
 def default_scale(d_nope: int = D_NOPE, d_rope: int = D_ROPE) -> float:
@@ -292,3 +303,60 @@ def cache_counts(n_heads=N_HEADS, d_nope=D_NOPE, d_rope=D_ROPE, d_latent=D_LATEN
     naive = n_heads * (d_nope + d_rope + d_v)     # expanded 192-wide K plus V
     return {"mha": mha, "mla": mla, "naive": naive, "reduction": 1.0 - mla / mha}
 
+
+
+# ----------------------------------------------------------------------------
+# Cache-append producer ([P5] 2.2: c_t^KV = W^DKV h_t, the short joint latent
+# each token caches; [P5] 2.3: the decoupled position branch keeps one small
+# key k^R shared by all heads, rotated by RoPE; [P3] MLA paragraphs: per token
+# and layer only c_KV in R^512 and the rotated k_R in R^64 are cached).
+
+def rope_inv_freq(d_rope=D_ROPE, base=ROPE_BASE):
+    """Angular frequency of pair i: base^(-2i/d_rope), i = 0 .. d_rope/2 - 1."""
+    i = np.arange(d_rope // 2, dtype=np.float64)
+    return base ** (-2.0 * i / d_rope)
+
+
+def rope_rotate(x, pos, base=ROPE_BASE):
+    """Rotary embedding of x [..., d] at integer positions pos (broadcast over
+    the leading axes): pair (x_2i, x_2i+1) turns counter-clockwise by
+    pos * theta_i, i.e. (x_2i cos - x_2i+1 sin, x_2i sin + x_2i+1 cos)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def append_rows(hidden, w_dkv, w_kr, positions, base=ROPE_BASE):
+    """Cache rows of new tokens, fp64: [c_KV = W_DKV h ; k_R = RoPE(W_KR h, pos)].
+
+    hidden [n, d_hidden], w_dkv [d_latent, d_hidden], w_kr [d_rope, d_hidden],
+    positions [n] (each token's index in its sequence). Returns [n, d_latent +
+    d_rope] in the cache's row order [c_KV | k_R]."""
+    hidden = np.asarray(hidden, dtype=np.float64)
+    c = hidden @ np.asarray(w_dkv, dtype=np.float64).T
+    k = rope_rotate(hidden @ np.asarray(w_kr, dtype=np.float64).T, positions, base)
+    return np.concatenate([c, k], axis=-1)
+
+
+def append_positions(seq_lens, q_tokens):
+    """Position of new token i of sequence b: L_b - Sq + i, as [B, Sq] (the new
+    tokens are the last Sq of each sequence, counted in L_b)."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    return lens[:, None] - q_tokens + np.arange(q_tokens)[None, :]
+
+
+def append_batch(hidden_bits, w_dkv_bits, w_kr_bits, seq_lens, q_tokens, base=ROPE_BASE):
+    """Exact (fp64) rows the producer writes for a batch: hidden bf16 bits
+    [B, Sq, d_hidden] -> [B, Sq, d_latent + d_rope]."""
+    h = bf16_bits_to_f64(hidden_bits)
+    n_b, sq, d_h = h.shape
+    pos = append_positions(seq_lens, q_tokens)
+    rows = append_rows(h.reshape(n_b * sq, d_h), bf16_bits_to_f64(w_dkv_bits),
+                       bf16_bits_to_f64(w_kr_bits), pos.reshape(-1), base)
+    return rows.reshape(n_b, sq, -1)

@@ -77,3 +77,46 @@ def test_unshifted_merge_weights_are_caught():
     bad = sum(o for o, _, _ in parts) / sum(l for _, _, l in parts)
     assert np.max(np.abs(bad - o_lat[0, 0])) > 1e-3
     assert np.max(np.abs(orc.merge_partials(parts) - o_lat[0, 0])) < 1e-12
+
+
+# ---- cache-append producer: planted mistakes in the rotary embedding must
+# move it away from the library rotary embedding it is pinned to
+
+def _rope_gap(monkeypatch, patch):
+    pytest.importorskip("transformers")
+    from tests.test_oracle_append import _library_rope
+    x = np.random.default_rng(8).standard_normal((6, 64))
+    pos = np.array([1, 2, 7, 31, 63, 500])
+    want = _library_rope(x, pos, 10000.0)
+    with monkeypatch.context() as m:
+        patch(m)
+        got = orc.rope_rotate(x, pos)
+    return np.max(np.abs(got - want))
+
+
+def test_rope_frequency_exponent_mistake_is_caught(monkeypatch):
+    def patch(m):
+        m.setattr(orc, "rope_inv_freq",
+                  lambda d=64, base=10000.0: base ** (-np.arange(d // 2, dtype=np.float64) / d))
+    assert _rope_gap(monkeypatch, patch) > 1e-2
+
+
+def test_rope_clockwise_rotation_is_caught(monkeypatch):
+    real = orc.rope_rotate
+    def patch(m):
+        m.setattr(orc, "rope_rotate", lambda x, pos, base=10000.0: real(x, -np.asarray(pos), base))
+    assert _rope_gap(monkeypatch, patch) > 1e-2
+
+
+def test_rope_half_split_pairing_is_caught(monkeypatch):
+    real = orc.rope_rotate
+    def half_split(x, pos, base=10000.0):
+        x = np.asarray(x, dtype=np.float64)
+        d = x.shape[-1]
+        inter = np.empty_like(x)
+        inter[..., 0::2], inter[..., 1::2] = x[..., : d // 2], x[..., d // 2:]
+        y = real(inter, pos, base)
+        return np.concatenate([y[..., 0::2], y[..., 1::2]], axis=-1)
+    def patch(m):
+        m.setattr(orc, "rope_rotate", half_split)
+    assert _rope_gap(monkeypatch, patch) > 1e-2
