@@ -137,6 +137,56 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* ar
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]);
 
+/* ---- Cache-append producer ------------------------------------------------
+ *
+ * Writes the cache rows of a decode step's new tokens: per token the short
+ * joint latent c_KV = W_DKV h (7168 -> 512) and the head-shared position key
+ * k_R = RoPE(W_KR h, pos) (7168 -> 64) ("DeepSeek-V3" article at m.lsln.cn,
+ * sections 2.2 and 2.3: c_t^KV = W^DKV h_t, and a small decoupled key k^R
+ * shared by the heads that carries the rotary position). New token i of
+ * sequence b sits at pos = seq_lens[b] - q_tokens + i (the same counting as
+ * mla_decode_run) and is stored, as bf16 rounded to nearest (ties to even),
+ * in block block_table[b, pos / 64], slot pos % 64, as [c_KV | k_R].
+ *
+ * RoPE: consecutive pairs (x_2i, x_2i+1) of W_KR h turn counter-clockwise by
+ * the angle pos * rope_base^(-2i/64), i = 0..31 (the pages name the rotary
+ * embedding without a formula; this is its own definition, no length
+ * scaling). Angles are formed in fp64.
+ *
+ * Layouts (row-major, device memory, borrowed):
+ *   hidden   bf16 [B, Sq, 7168]
+ *   w_dkv    bf16 [512, 7168]
+ *   w_kr     bf16 [64, 7168]
+ *   kv_cache bf16 [num_blocks, 64, 576]: only the new tokens' rows are written;
+ *            a token whose position or block id is out of range is skipped
+ * Numerics: bf16 products exact, fp32 accumulation, one rounding to bf16 of
+ * the finished value (the result is within one bf16 step of the exact one).
+ * The call enqueues two kernels on `stream`, never allocates or
+ * synchronises; `workspace` (fp32 partial sums, mla_cache_append_workspace_size
+ * bytes, 256-byte aligned) must not be shared by overlapping calls. Errors as
+ * for mla_decode_run. */
+typedef struct mla_append_args {
+  const void* hidden;          /* bf16 [B, Sq, 7168] */
+  const void* w_dkv;           /* bf16 [512, 7168] */
+  const void* w_kr;            /* bf16 [64, 7168] */
+  void* kv_cache;              /* bf16 [num_blocks, 64, 576]; rows written */
+  const int32_t* block_table;  /* int32 [B, max_blocks_per_seq] */
+  const int32_t* seq_lens;     /* int32 [B], counting the new tokens */
+  int64_t num_blocks;          /* blocks in kv_cache */
+  int32_t batch;               /* 1 <= B <= 1000000 */
+  int32_t q_tokens;            /* Sq: 1 or 2, <= max_q_tokens */
+  int32_t max_blocks_per_seq;  /* row stride of block_table */
+  float rope_base;             /* <= 0 selects 10000 */
+} mla_append_args;
+
+/* Bytes of workspace mla_cache_append needs for B * Sq new tokens. */
+int mla_cache_append_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                                    size_t* bytes);
+
+/* Enqueue the cache-append producer for one decode step (see above). */
+int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* args, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Release a context (NULL is accepted). */
 void mla_decode_destroy(mla_decode_ctx* ctx);
 

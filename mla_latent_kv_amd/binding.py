@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 
 MLA_OK = 0
 N_HEADS, D_NOPE, D_ROPE, D_LATENT, D_V, BLOCK = 128, 128, 64, 512, 128, 64
+D_HIDDEN = 7168
 
 
 class MlaDecodeConfig(ctypes.Structure):
@@ -50,6 +51,22 @@ class MlaDecodeArgs(ctypes.Structure):
     ]
 
 
+class MlaAppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_void_p),
+        ("w_dkv", ctypes.c_void_p),
+        ("w_kr", ctypes.c_void_p),
+        ("kv_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("batch", ctypes.c_int32),
+        ("q_tokens", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -76,6 +93,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                             ctypes.POINTER(ctypes.c_void_p)]
     lib.mla_decode_run_profiled.restype = ctypes.c_int
+    lib.mla_cache_append_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_cache_append_workspace_size.restype = ctypes.c_int
+    lib.mla_cache_append.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaAppendArgs),
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_cache_append.restype = ctypes.c_int
     lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
     lib.mla_decode_destroy.restype = None
     lib.mla_decode_status_string.argtypes = [ctypes.c_int]
@@ -179,6 +202,57 @@ def mla_decode_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_len
     return out
 
 
+def mla_cache_append_workspace_size(ctx, batch: int, q_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mla_cache_append_workspace_size(ctx, int(batch), int(q_tokens),
+                                                          ctypes.byref(n)),
+           "mla_cache_append_workspace_size")
+    return n.value
+
+
+def mla_cache_append(ctx, hidden, w_dkv, w_kr, kv_cache, block_table, seq_lens,
+                     rope_base: float = 0.0, workspace=None, stream=None):
+    """Enqueue the cache-append producer: writes the new tokens' rows
+    [W_DKV h | RoPE(W_KR h, pos)] (bf16) into ``kv_cache`` in place and returns it.
+
+    hidden [B, Sq, 7168], w_dkv [512, 7168], w_kr [64, 7168], kv_cache
+    [num_blocks, 64, 576] (bf16 or 16-bit integer views of the bits),
+    block_table int32 [B, max_blocks_per_seq], seq_lens int32 [B] counting the
+    new tokens. ``rope_base`` <= 0 selects 10000.
+    """
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _require(hidden, "hidden", b16, 3)
+    _require(w_dkv, "w_dkv", b16, 2)
+    _require(w_kr, "w_kr", b16, 2)
+    _require(kv_cache, "kv_cache", b16, 3)
+    _require(block_table, "block_table", (torch.int32,), 2)
+    _require(seq_lens, "seq_lens", (torch.int32,), 1)
+    B, Sq = hidden.shape[0], hidden.shape[1]
+    if hidden.shape[2] != D_HIDDEN:
+        raise ValueError("hidden must be [B, Sq, 7168]")
+    if tuple(w_dkv.shape) != (D_LATENT, D_HIDDEN) or tuple(w_kr.shape) != (D_ROPE, D_HIDDEN):
+        raise ValueError("w_dkv / w_kr must be [512, 7168] / [64, 7168]")
+    if tuple(kv_cache.shape[1:]) != (BLOCK, D_LATENT + D_ROPE):
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table / seq_lens batch mismatch")
+    need = mla_cache_append_workspace_size(ctx, B, Sq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
+    args = MlaAppendArgs(hidden.data_ptr(), w_dkv.data_ptr(), w_kr.data_ptr(), kv_cache.data_ptr(),
+                         block_table.data_ptr(), seq_lens.data_ptr(), kv_cache.shape[0], B, Sq,
+                         block_table.shape[1], float(rope_base))
+    _check(load_library().mla_cache_append(ctx, ctypes.byref(args), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(),
+                                           ctypes.c_void_p(s.cuda_stream)),
+           "mla_cache_append")
+    return kv_cache
+
+
 class MLADecoder:
     """Owns a context; ``decoder(...)`` forwards to mla_decode_run."""
 
@@ -192,6 +266,10 @@ class MLADecoder:
 
     def __call__(self, *args, **kw):
         return mla_decode_run(self.ctx, *args, **kw)
+
+    def append(self, *args, **kw):
+        """Forwards to mla_cache_append (the new tokens' cache rows)."""
+        return mla_cache_append(self.ctx, *args, **kw)
 
     def close(self):
         if self.ctx:

@@ -1,6 +1,7 @@
 // C ABI of the MLA decode library (declared in include/mla_decode.h):
-// argument validation, workspace sizing and the launch sequence
-// plan -> absorb -> attention -> merge, all on the caller's stream.
+// argument validation, workspace sizing and the launch sequences
+// plan -> absorb -> attention -> merge (decode) and product -> finish (cache
+// append), all on the caller's stream.
 #include <math.h>
 #include <string.h>
 
@@ -164,6 +165,45 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* a,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]) {
   return run_impl(ctx, a, workspace, workspace_bytes, stream, events);
+}
+
+int mla_cache_append_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                                    size_t* bytes) {
+  if (!ctx || !bytes || batch < 1 || batch > mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
+  if (q_tokens < 1 || q_tokens > ctx->cfg.max_q_tokens) return MLA_ERR_INVALID_ARG;
+  *bytes = mla::append_workspace_bytes(batch * q_tokens);
+  return MLA_OK;
+}
+
+int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* a, void* workspace,
+                     size_t workspace_bytes, void* stream_handle) {
+  if (!ctx || !a) return MLA_ERR_INVALID_ARG;
+  if (!a->hidden || !a->w_dkv || !a->w_kr || !a->kv_cache || !a->block_table || !a->seq_lens)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->batch > mla::kMaxBatch || a->q_tokens < 1 ||
+      a->q_tokens > ctx->cfg.max_q_tokens || a->num_blocks < 1 || a->max_blocks_per_seq < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!(a->rope_base == a->rope_base)) return MLA_ERR_INVALID_ARG;   // NaN
+  if (!aligned16(a->hidden) || !aligned16(a->w_dkv) || !aligned16(a->w_kr) ||
+      !aligned16(a->kv_cache) || !aligned16(a->block_table) || !aligned16(a->seq_lens))
+    return MLA_ERR_MISALIGNED;
+  const size_t need = mla::append_workspace_bytes(a->batch * a->q_tokens);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return MLA_ERR_WORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  const double base = a->rope_base > 0.f ? (double)a->rope_base : 10000.0;
+  const int status =
+      mla::launch_append((const uint16_t*)a->hidden, (const uint16_t*)a->w_dkv,
+                         (const uint16_t*)a->w_kr, (uint16_t*)a->kv_cache, a->block_table,
+                         a->seq_lens, a->num_blocks, a->max_blocks_per_seq, a->batch,
+                         a->q_tokens, base, (float*)workspace, stream) == hipSuccess
+          ? MLA_OK
+          : MLA_ERR_HIP;
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
 }
 
 void mla_decode_destroy(mla_decode_ctx* ctx) { delete ctx; }

@@ -18,6 +18,8 @@ constexpr int kDV = 128;
 constexpr int kRow = kDLat + kDRope;    // 576 cached elements per token
 constexpr int kRowBytes = kRow * 2;     // 1152
 constexpr int kBlock = 64;              // tokens per cache block
+constexpr int kDHidden = 7168;          // model width, input of the cache-append producer
+constexpr int kAppKSplit = 16;          // K-chunks of the cache-append product
 
 // Work decomposition of the attention pass.
 constexpr int kTileTok = 32;            // cached tokens per LDS tile
@@ -33,6 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -108,6 +111,15 @@ struct AttnArgs {
   float scale_log2;   // softmax scale * log2(e)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+// cache-append producer (two launches): fp32 partials of W h per K-chunk in
+// `part` (append_workspace_bytes), then the sums, RoPE, bf16 rounding and the
+// writes of the new tokens' cache rows
+size_t append_workspace_bytes(int rows);
+hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_dkv, const uint16_t* w_kr,
+                         uint16_t* cache, const int32_t* block_table, const int32_t* seq_lens,
+                         long long num_blocks, int max_blocks_per_seq, int batch, int q_tokens,
+                         double rope_base, float* part, hipStream_t stream);
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const SeqInfo* seqinfo,
                         const uint16_t* w_uv, float* out, int batch, int q_tokens,
                         hipStream_t stream);

@@ -139,3 +139,21 @@ def make_batch(spec: Spec, seed: int, poison: bool = True) -> dict:
         "cache": cache, "block_table": table, "seq_lens": lens,
         "max_seq_len": max_seq, "block_size": bs, "spec": spec,
     }
+
+
+D_HIDDEN = 7168   # model width (input of the cache-append producer)
+
+
+def make_append_inputs(batch: int, q_tokens: int, seed: int, d_hidden: int = D_HIDDEN,
+                       d_latent: int = 512, d_rope: int = 64) -> dict:
+    """Inputs of the cache-append producer as bf16 bits: hidden [B, Sq, d_hidden]
+    ~ N(0, 1), w_dkv [d_latent, d_hidden] and w_kr [d_rope, d_hidden] ~ N(0,
+    1/d_hidden), so each appended value has unit variance like the synthetic
+    cache rows."""
+    r_h, r_d, r_k = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3))
+    w_std = 1.0 / np.sqrt(d_hidden)
+    return {
+        "hidden": _normal_bits(r_h, (batch, q_tokens, d_hidden)),
+        "w_dkv": _normal_bits(r_d, (d_latent, d_hidden), std=w_std),
+        "w_kr": _normal_bits(r_k, (d_rope, d_hidden), std=w_std),
+    }

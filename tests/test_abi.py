@@ -21,10 +21,11 @@ def _lib():
 
 def test_every_declared_symbol_is_exported():
     src = open(HEADER).read()
-    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(mla_decode_\w+)\s*\(", src, re.M))
+    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(mla_\w+)\s*\(", src, re.M))
     assert declared == {"mla_decode_init", "mla_decode_workspace_size", "mla_decode_run",
                         "mla_decode_run_profiled", "mla_decode_destroy",
-                        "mla_decode_status_string"}
+                        "mla_decode_status_string", "mla_cache_append",
+                        "mla_cache_append_workspace_size"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -77,3 +78,14 @@ def test_workspace_layout_bounds():
         chunks = int(sum(-(-int(l) // C) for l in lens))
         cap = min(target + B, B * -(-max_len // 64))
         assert chunks <= cap
+
+
+def test_cache_append_rejects_nulls_before_any_device_call():
+    import ctypes
+    from mla_latent_kv_amd import binding
+    lib = _lib()
+    n = ctypes.c_size_t()
+    assert lib.mla_cache_append_workspace_size(None, 4, 1, ctypes.byref(n)) == -1
+    args = binding.MlaAppendArgs()
+    assert lib.mla_cache_append(None, ctypes.byref(args), None, 0, None) == -1
+    assert lib.mla_cache_append(None, None, None, 0, None) == -1
