@@ -36,6 +36,7 @@ METRIC = "decode query-tokens/s + latent-cache HBM TB/s, MLA absorb B=32 L=4K"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
+APPEND_WEIGHT_BYTES = (512 + 64) * 7168 * 2   # W_DKV and W_KR, bf16
 
 # HBM traffic of one attention launch from two rocprofv3 --pmc runs of this
 # script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
@@ -133,6 +134,65 @@ def cpu_baseline(batch, budget_s: float, max_seqs: int) -> dict:
                       f"tokens x 128 heads), fp64 NumPy naive path, {dt:.1f} s"}
 
 
+def time_cache_append(lib, dec, d, B, Sq, stream, args) -> dict:
+    """The cache-append producer on the same batch shape (its new tokens'
+    rows), HIP events around `steps` calls on the launch stream. The weights
+    rotate over enough copies (8.3 MB each) to exceed the Infinity Cache, as
+    successive layers' weights would."""
+    import torch
+    from mla_latent_kv_amd import binding, synth
+    n_w = max(1, math.ceil(MALL_BYTES / (APPEND_WEIGHT_BYTES)) + 1)
+    inp = synth.make_append_inputs(B, Sq, seed=1000)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    hid = bf16(inp["hidden"])
+    ws = [(bf16(inp["w_dkv"]), bf16(inp["w_kr"]))]
+    for _ in range(n_w - 1):
+        ws.append((ws[0][0].clone(), ws[0][1].clone()))
+    cache = d["kv_cache"].clone()   # the decode inputs stay as they were
+    need = binding.mla_cache_append_workspace_size(dec.ctx, B, Sq)
+    wsp = torch.empty(need, dtype=torch.uint8, device="cuda")
+    cargs = [binding.MlaAppendArgs(hid.data_ptr(), wd.data_ptr(), wk.data_ptr(), cache.data_ptr(),
+                                   d["block_table"].data_ptr(), d["seq_lens"].data_ptr(),
+                                   cache.shape[0], B, Sq, d["block_table"].shape[1], 0.0)
+             for wd, wk in ws]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(i):
+        rc = lib.mla_cache_append(dec.ctx, ctypes.byref(cargs[i % n_w]), ctypes.c_void_p(wsp.data_ptr()),
+                                  need, sh)
+        if rc != 0:
+            raise RuntimeError(binding.mla_decode_status_string(rc))
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    rows = B * Sq
+    nbytes = APPEND_WEIGHT_BYTES + rows * 7168 * 2 + rows * 1152
+    out = {"us_per_call": us, "new_tokens": rows, "rotating_weight_sets": n_w,
+           "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+           "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "launches": 2}
+    if not args.no_cpu:
+        # the oracle's fp64 rows for the same tokens, timed on the host
+        from oracle import mla_oracle as orc
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < 1.0:
+            orc.append_batch(inp["hidden"], inp["w_dkv"], inp["w_kr"],
+                             d["seq_lens"].cpu().numpy(), Sq)
+            reps += 1
+        out["cpu_oracle_us_per_call"] = (time.perf_counter() - t0) / reps * 1e6
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +202,8 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the cache-append producer's timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -272,6 +334,8 @@ def main() -> int:
         },
         "whole_step_roofline_frac": work["total_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
     }
+    if not args.no_append:
+        result["cache_append"] = time_cache_append(lib, dec, d, B, Sq, stream, args)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0])
     print(json.dumps(result), flush=True)
