@@ -40,6 +40,8 @@ Readings where the pages are silent or garbled (each is repeated in the design doc):
 * the appended latent is c_KV = W_DKV h exactly as the pages write it (no
   normalisation of c_KV), and k_R = RoPE(W_KR h) at the new token's position
   L - Sq + i.
+* output projection: W_O in R^{7168 x 16384} maps the heads' outputs,
+  concatenated head-major (index h * 128 + v), back to the model width.
 * with Sq new tokens per sequence (all already in the cache, counted in L),
   query i sees cached positions j <= L - Sq + i.
 * k_R is one 64-d key per token shared by every head ([P5] section 2.3).
@@ -360,3 +362,16 @@ def append_batch(hidden_bits, w_dkv_bits, w_kr_bits, seq_lens, q_tokens, base=RO
     rows = append_rows(h.reshape(n_b * sq, d_h), bf16_bits_to_f64(w_dkv_bits),
                        bf16_bits_to_f64(w_kr_bits), pos.reshape(-1), base)
     return rows.reshape(n_b, sq, -1)
+
+
+# ----------------------------------------------------------------------------
+# Output projection (the last step of the attention block, [P3] MLA state
+# flow: the attention output goes through an output projection matrix back to
+# the model width).
+
+def output_project(o, w_o):
+    """y[t, :] = W_O concat_h(o[t, h, :]) for attention outputs o [n, H, d_v]
+    (or already flat [n, H * d_v]) and W_O [d_model, H * d_v], fp64."""
+    o = np.asarray(o, dtype=np.float64)
+    flat = o.reshape(o.shape[0], -1)
+    return flat @ np.asarray(w_o, dtype=np.float64).T

@@ -1,4 +1,4 @@
-"""Pins of the oracle's cache-append producer (CPU only).
+"""Pins of the oracle's cache-append producer and output projection (CPU only).
 
 The pages give c_KV = W_DKV h and a RoPE-rotated, head-shared k_R without the
 rotary formula, so the rotation is pinned by the properties that define a
@@ -7,7 +7,9 @@ angles, scores that depend only on the relative position) and against an
 independent library implementation (transformers' Llama rotary embedding,
 whose half-split pairing equals the consecutive-pair one after de-interleaving
 the 64 channels). The projection and the row layout are pinned by scalar
-brute force on tiny shapes.
+brute force on tiny shapes. The output projection W_O concat_h(o_h) is pinned
+by scalar brute force (which also fixes the head-major concatenation order),
+linearity and unit vectors.
 """
 
 import math
@@ -144,3 +146,34 @@ def test_append_batch_unit_hidden_selects_weight_columns():
     assert not np.allclose(rows[1, 0, orc.D_LATENT:], wk[:, 30])
     assert math.isclose(np.linalg.norm(rows[1, 0, orc.D_LATENT:]), np.linalg.norm(wk[:, 30]),
                         rel_tol=1e-13)
+
+
+# ---- output projection pins
+
+def test_output_project_scalar_brute_force_and_head_order():
+    r = _rng(9)
+    n, H, dv, dm = 2, 3, 4, 5
+    o = r.standard_normal((n, H, dv))
+    w = r.standard_normal((dm, H * dv))
+    y = orc.output_project(o, w)
+    for t in range(n):
+        for m in range(dm):
+            want = sum(w[m, h * dv + v] * o[t, h, v] for h in range(H) for v in range(dv))
+            assert abs(y[t, m] - want) < 1e-12
+    # a head's block of W_O acts only on that head's output
+    o2 = np.zeros_like(o)
+    o2[:, 1] = o[:, 1]
+    np.testing.assert_allclose(orc.output_project(o2, w), o[:, 1] @ w[:, dv:2 * dv].T,
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_output_project_linear_and_unit_columns():
+    r = _rng(10)
+    o1, o2 = r.standard_normal((2, 3, 8, 16))
+    w = r.standard_normal((12, 128))
+    np.testing.assert_allclose(orc.output_project(2 * o1 - 3 * o2, w),
+                               2 * orc.output_project(o1, w) - 3 * orc.output_project(o2, w),
+                               rtol=1e-12, atol=1e-12)
+    e = np.zeros((1, 8, 16))
+    e[0, 5, 7] = 1.0
+    np.testing.assert_array_equal(orc.output_project(e, w)[0], w[:, 5 * 16 + 7])
