@@ -187,6 +187,30 @@ int mla_cache_append_workspace_size(const mla_decode_ctx* ctx, int32_t batch, in
 int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* args, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* ---- Output projection -----------------------------------------------------
+ *
+ * y[t, :] = W_O x_t: the attention outputs of token t (the `out` of
+ * mla_decode_run, 128 heads x 128, concatenated head-major: index h * 128 + v)
+ * mapped back to the model width 7168 by one output projection matrix
+ * ("DeepSeek-V3" page at ailearn.mscapital.top, MLA state flow).
+ *
+ * Layouts (row-major, device memory, borrowed; 16-byte aligned):
+ *   x    fp32 [rows, 16384]      (mla_decode_run's out viewed as [B * Sq, 16384])
+ *   w_o  bf16 [7168, 16384]
+ *   y    fp32 [rows, 7168]       written
+ * Numerics: x enters the bf16 matrix cores as x = hi + lo (hi = bf16(x), lo =
+ * bf16(x - hi), together within 2^-17 of x); products are accumulated in fp32.
+ * One kernel on `stream`, no workspace, no allocation, no synchronisation.
+ * Errors as for mla_decode_run. */
+typedef struct mla_oproj_args {
+  const float* x;    /* fp32 [rows, 16384] */
+  const void* w_o;   /* bf16 [7168, 16384] */
+  float* y;          /* fp32 [rows, 7168] */
+  int32_t rows;      /* tokens, >= 1 */
+} mla_oproj_args;
+
+int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* args, void* stream);
+
 /* Release a context (NULL is accepted). */
 void mla_decode_destroy(mla_decode_ctx* ctx);
 

@@ -67,6 +67,15 @@ class MlaAppendArgs(ctypes.Structure):
     ]
 
 
+class MlaOprojArgs(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("w_o", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("rows", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -99,6 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_cache_append.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaAppendArgs),
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_cache_append.restype = ctypes.c_int
+    lib.mla_output_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaOprojArgs), ctypes.c_void_p]
+    lib.mla_output_project.restype = ctypes.c_int
     lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
     lib.mla_decode_destroy.restype = None
     lib.mla_decode_status_string.argtypes = [ctypes.c_int]
@@ -253,6 +264,28 @@ def mla_cache_append(ctx, hidden, w_dkv, w_kr, kv_cache, block_table, seq_lens,
     return kv_cache
 
 
+def mla_output_project(ctx, x, w_o, y=None, stream=None):
+    """Enqueue y = W_O x: x fp32 [T, 16384] (or mla_decode_run's out [B, Sq,
+    128, 128], viewed flat), w_o bf16 [7168, 16384]; returns y fp32 [T, 7168]."""
+    import torch
+    if x.dim() == 4:
+        x = x.reshape(-1, N_HEADS * D_V)
+    _require(x, "x", (torch.float32,), 2)
+    _require(w_o, "w_o", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    if x.shape[1] != N_HEADS * D_V or tuple(w_o.shape) != (D_HIDDEN, N_HEADS * D_V):
+        raise ValueError("x must be [T, 16384] and w_o [7168, 16384]")
+    if y is None:
+        y = torch.empty((x.shape[0], D_HIDDEN), dtype=torch.float32, device=x.device)
+    _require(y, "y", (torch.float32,), 2)
+    if tuple(y.shape) != (x.shape[0], D_HIDDEN):
+        raise ValueError("y must be [T, 7168] fp32")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    args = MlaOprojArgs(x.data_ptr(), w_o.data_ptr(), y.data_ptr(), x.shape[0])
+    _check(load_library().mla_output_project(ctx, ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)),
+           "mla_output_project")
+    return y
+
+
 class MLADecoder:
     """Owns a context; ``decoder(...)`` forwards to mla_decode_run."""
 
@@ -270,6 +303,10 @@ class MLADecoder:
     def append(self, *args, **kw):
         """Forwards to mla_cache_append (the new tokens' cache rows)."""
         return mla_cache_append(self.ctx, *args, **kw)
+
+    def output_project(self, *args, **kw):
+        """Forwards to mla_output_project (y = W_O x)."""
+        return mla_output_project(self.ctx, *args, **kw)
 
     def close(self):
         if self.ctx:

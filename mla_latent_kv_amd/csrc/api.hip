@@ -206,6 +206,21 @@ int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* a, void* 
   return status;
 }
 
+int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* a, void* stream_handle) {
+  if (!ctx || !a || !a->x || !a->w_o || !a->y) return MLA_ERR_INVALID_ARG;
+  if (a->rows < 1 || a->rows > 2 * mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(a->x) || !aligned16(a->w_o) || !aligned16(a->y)) return MLA_ERR_MISALIGNED;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  const int status = mla::launch_oproj(a->x, (const uint16_t*)a->w_o, a->y, a->rows, stream) == hipSuccess
+                         ? MLA_OK
+                         : MLA_ERR_HIP;
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
+}
+
 void mla_decode_destroy(mla_decode_ctx* ctx) { delete ctx; }
 
 }  // extern "C"

@@ -115,6 +115,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 // cache-append producer (two launches): fp32 partials of W h per K-chunk in
 // `part` (append_workspace_bytes), then the sums, RoPE, bf16 rounding and the
 // writes of the new tokens' cache rows
+// output projection y = W_O x (one launch): x fp32 [rows][16384], W_O bf16
+// [7168][16384], y fp32 [rows][7168]
+hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, hipStream_t stream);
+
 size_t append_workspace_bytes(int rows);
 hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_dkv, const uint16_t* w_kr,
                          uint16_t* cache, const int32_t* block_table, const int32_t* seq_lens,

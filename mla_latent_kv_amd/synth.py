@@ -157,3 +157,12 @@ def make_append_inputs(batch: int, q_tokens: int, seed: int, d_hidden: int = D_H
         "w_dkv": _normal_bits(r_d, (d_latent, d_hidden), std=w_std),
         "w_kr": _normal_bits(r_k, (d_rope, d_hidden), std=w_std),
     }
+
+
+def make_oproj_inputs(rows: int, seed: int, d_in: int = 128 * 128, d_model: int = D_HIDDEN) -> dict:
+    """Inputs of the output projection: x fp32 [rows, d_in] ~ N(0, 1) (the
+    attention outputs it consumes are fp32) and w_o as bf16 bits [d_model,
+    d_in] ~ N(0, 1/d_in)."""
+    r_x, r_w = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(2))
+    return {"x": r_x.standard_normal((rows, d_in), dtype=np.float32),
+            "w_o": _normal_bits(r_w, (d_model, d_in), std=1.0 / np.sqrt(d_in))}

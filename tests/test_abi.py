@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
     assert declared == {"mla_decode_init", "mla_decode_workspace_size", "mla_decode_run",
                         "mla_decode_run_profiled", "mla_decode_destroy",
                         "mla_decode_status_string", "mla_cache_append",
-                        "mla_cache_append_workspace_size"}
+                        "mla_cache_append_workspace_size", "mla_output_project"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -89,3 +89,12 @@ def test_cache_append_rejects_nulls_before_any_device_call():
     args = binding.MlaAppendArgs()
     assert lib.mla_cache_append(None, ctypes.byref(args), None, 0, None) == -1
     assert lib.mla_cache_append(None, None, None, 0, None) == -1
+
+
+def test_output_project_rejects_nulls_before_any_device_call():
+    import ctypes
+    from mla_latent_kv_amd import binding
+    lib = _lib()
+    args = binding.MlaOprojArgs()
+    assert lib.mla_output_project(None, ctypes.byref(args), None) == -1
+    assert lib.mla_output_project(None, None, None) == -1
