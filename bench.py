@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 APPEND_WEIGHT_BYTES = (512 + 64) * 7168 * 2   # W_DKV and W_KR, bf16
+OPROJ_WEIGHT_BYTES = 7168 * 16384 * 2         # W_O, bf16
 
 # HBM traffic of one attention launch from two rocprofv3 --pmc runs of this
 # script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
@@ -193,6 +194,55 @@ def time_cache_append(lib, dec, d, B, Sq, stream, args) -> dict:
     return out
 
 
+def time_output_project(lib, dec, B, Sq, stream, args) -> dict:
+    """The output projection for the batch's tokens (y = W_O x, 235 MB of
+    weights), HIP events around `steps` calls; two weight copies alternate so
+    the Infinity Cache cannot hold the stream."""
+    import torch
+    from mla_latent_kv_amd import binding, synth
+    rows = B * Sq
+    inp = synth.make_oproj_inputs(rows, seed=2000)
+    x = torch.from_numpy(inp["x"]).cuda()
+    w0 = torch.from_numpy(np.ascontiguousarray(inp["w_o"]).view(np.int16)).cuda().view(torch.bfloat16)
+    n_w = max(2, math.ceil(MALL_BYTES / OPROJ_WEIGHT_BYTES) + 1)
+    ws = [w0] + [w0.clone() for _ in range(n_w - 1)]
+    y = torch.empty((rows, 7168), dtype=torch.float32, device="cuda")
+    cargs = [binding.MlaOprojArgs(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows) for w in ws]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(i):
+        rc = lib.mla_output_project(dec.ctx, ctypes.byref(cargs[i % n_w]), sh)
+        if rc != 0:
+            raise RuntimeError(binding.mla_decode_status_string(rc))
+
+    for i in range(max(2, args.warmup // 4)):
+        call(i)
+    torch.cuda.synchronize()
+    n = max(4, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    nbytes = OPROJ_WEIGHT_BYTES + rows * 16384 * 4 + rows * 7168 * 4
+    out = {"us_per_call": us, "tokens": rows, "rotating_weight_sets": n_w, "calls": n,
+           "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+           "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "launches": 1}
+    if not args.no_cpu:
+        from oracle import mla_oracle as orc
+        w64 = orc.bf16_bits_to_f64(inp["w_o"])
+        x64 = inp["x"].astype(np.float64)
+        reps, t0 = 0, time.perf_counter()
+        while reps < 2 or time.perf_counter() - t0 < 1.0:
+            orc.output_project(x64, w64)
+            reps += 1
+        out["cpu_oracle_us_per_call"] = (time.perf_counter() - t0) / reps * 1e6
+        del w64
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,7 +253,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-append", action="store_true",
-                    help="skip the cache-append producer's timing")
+                    help="skip the timings of the cache-append producer and the output projection")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -336,6 +386,7 @@ def main() -> int:
     }
     if not args.no_append:
         result["cache_append"] = time_cache_append(lib, dec, d, B, Sq, stream, args)
+        result["output_project"] = time_output_project(lib, dec, B, Sq, stream, args)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0])
     print(json.dumps(result), flush=True)
