@@ -42,6 +42,12 @@ Readings where the pages are silent or garbled (each is repeated in the design doc):
   L - Sq + i.
 * output projection: W_O in R^{7168 x 16384} maps the heads' outputs,
   concatenated head-major (index h * 128 + v), back to the model width.
+* query side: the query is compressed to rank 1536 ([P3] configuration
+  table): c_Q = W_DQ h (7168 -> 1536), then per head q = W_UQ[h] c_Q
+  (1536 -> 192), rows 0..127 the non-positional part q_nope and rows
+  128..191 the position part, rotated like k_R at the token's position:
+  q_pe = RoPE(q[128:], L - Sq + i). No normalisation of c_Q (the pages give
+  none).
 * with Sq new tokens per sequence (all already in the cache, counted in L),
   query i sees cached positions j <= L - Sq + i.
 * k_R is one 64-d key per token shared by every head ([P5] section 2.3).
@@ -375,3 +381,35 @@ def output_project(o, w_o):
     o = np.asarray(o, dtype=np.float64)
     flat = o.reshape(o.shape[0], -1)
     return flat @ np.asarray(w_o, dtype=np.float64).T
+
+
+# ----------------------------------------------------------------------------
+# Query side ([P3] configuration table: Q compression rank 1536, per-head
+# non-positional width 128 and RoPE width 64; [P5] 2.3: a small per-head
+# position query q^R, rotated like the shared k^R).
+
+D_QRANK = 1536
+
+
+def query_project(hidden, w_dq, w_uq, positions, base=ROPE_BASE, d_nope=D_NOPE, d_rope=D_ROPE):
+    """q_nope [n, H, d_nope] and q_pe [n, H, d_rope] of new tokens, fp64.
+
+    hidden [n, d_hidden], w_dq [d_q, d_hidden], w_uq [H, d_nope + d_rope, d_q],
+    positions [n]."""
+    hidden = np.asarray(hidden, dtype=np.float64)
+    c_q = hidden @ np.asarray(w_dq, dtype=np.float64).T                  # [n, d_q]
+    q = np.einsum("hrq,nq->nhr", np.asarray(w_uq, dtype=np.float64), c_q)  # [n, H, 192]
+    q_nope = q[..., :d_nope]
+    q_pe = rope_rotate(q[..., d_nope:], np.asarray(positions)[:, None], base)
+    return q_nope, q_pe
+
+
+def query_batch(hidden_bits, w_dq_bits, w_uq_bits, seq_lens, q_tokens, base=ROPE_BASE):
+    """Exact q_nope [B, Sq, H, 128] and q_pe [B, Sq, H, 64] for a batch (bf16
+    bit inputs; positions L_b - Sq + i)."""
+    h = bf16_bits_to_f64(hidden_bits)
+    n_b, sq, d_h = h.shape
+    pos = append_positions(seq_lens, q_tokens).reshape(-1)
+    qn, qp = query_project(h.reshape(n_b * sq, d_h), bf16_bits_to_f64(w_dq_bits),
+                           bf16_bits_to_f64(w_uq_bits), pos, base)
+    return qn.reshape(n_b, sq, *qn.shape[1:]), qp.reshape(n_b, sq, *qp.shape[1:])

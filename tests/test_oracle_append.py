@@ -1,4 +1,5 @@
-"""Pins of the oracle's cache-append producer and output projection (CPU only).
+"""Pins of the oracle's cache-append producer, query side and output projection
+(CPU only).
 
 The pages give c_KV = W_DKV h and a RoPE-rotated, head-shared k_R without the
 rotary formula, so the rotation is pinned by the properties that define a
@@ -177,3 +178,46 @@ def test_output_project_linear_and_unit_columns():
     e = np.zeros((1, 8, 16))
     e[0, 5, 7] = 1.0
     np.testing.assert_array_equal(orc.output_project(e, w)[0], w[:, 5 * 16 + 7])
+
+
+# ---- query side pins
+
+def test_query_project_scalar_brute_force():
+    r = _rng(11)
+    n, d_h, d_q, H, dn, dr = 2, 6, 4, 3, 2, 4
+    h = r.standard_normal((n, d_h))
+    w_dq = r.standard_normal((d_q, d_h))
+    w_uq = r.standard_normal((H, dn + dr, d_q))
+    pos = np.array([0, 7])
+    qn, qp = orc.query_project(h, w_dq, w_uq, pos, base=50.0, d_nope=dn, d_rope=dr)
+    for t in range(n):
+        c = [sum(w_dq[j, k] * h[t, k] for k in range(d_h)) for j in range(d_q)]
+        for hh in range(H):
+            full = [sum(w_uq[hh, rr, j] * c[j] for j in range(d_q)) for rr in range(dn + dr)]
+            np.testing.assert_allclose(qn[t, hh], full[:dn], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(qp[t, hh], orc.rope_rotate(np.array(full[dn:]), pos[t], 50.0),
+                                       rtol=0, atol=1e-12)
+            if pos[t] == 0:
+                np.testing.assert_allclose(qp[t, hh], full[dn:], rtol=0, atol=1e-12)
+
+
+def test_query_and_key_rotations_give_relative_scores():
+    """q_pe . k_R of the same projected vectors depends only on the distance
+    between the query's and the key's positions."""
+    r = _rng(12)
+    qv, kv = r.standard_normal(64), r.standard_normal(64)
+    s1 = orc.rope_rotate(qv, 1000) @ orc.rope_rotate(kv, 990)
+    s2 = orc.rope_rotate(qv, 40) @ orc.rope_rotate(kv, 30)
+    assert abs(s1 - s2) < 1e-10
+
+
+def test_query_project_linear_in_hidden():
+    r = _rng(13)
+    h1, h2 = r.standard_normal((2, 3, 20))
+    w_dq, w_uq = r.standard_normal((8, 20)), r.standard_normal((2, 6, 8))
+    pos = np.array([1, 2, 300])
+    a = orc.query_project(h1 - 2 * h2, w_dq, w_uq, pos, d_nope=2, d_rope=4)
+    b1 = orc.query_project(h1, w_dq, w_uq, pos, d_nope=2, d_rope=4)
+    b2 = orc.query_project(h2, w_dq, w_uq, pos, d_nope=2, d_rope=4)
+    for i in range(2):
+        np.testing.assert_allclose(a[i], b1[i] - 2 * b2[i], rtol=1e-12, atol=1e-12)
