@@ -187,6 +187,48 @@ int mla_cache_append_workspace_size(const mla_decode_ctx* ctx, int32_t batch, in
 int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* args, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* ---- Query side ------------------------------------------------------------
+ *
+ * The decode's queries from the new tokens' hidden states: the query is
+ * compressed to rank 1536 and each head carries 128 non-positional and 64
+ * position dimensions ("DeepSeek-V3" page at ailearn.mscapital.top,
+ * configuration table); the small per-head position query is rotated like
+ * the shared position key ("DeepSeek-V3" article at m.lsln.cn, section 2.3):
+ *   c_Q = W_DQ h (7168 -> 1536);  q[h] = W_UQ[h] c_Q (1536 -> 192)
+ *   q_nope[h] = q[h][0..127];  q_pe[h] = RoPE(q[h][128..191], pos)
+ * with pos = seq_lens[b] - q_tokens + i and the RoPE of mla_cache_append. The
+ * outputs are exactly mla_decode_run's q_nope and q_pe inputs.
+ *
+ * Layouts (row-major, device memory, borrowed; 16-byte aligned):
+ *   hidden  bf16 [B, Sq, 7168]
+ *   w_dq    bf16 [1536, 7168]
+ *   w_uq    bf16 [128, 192, 1536]  per head: 128 non-positional rows, then 64
+ *                                  position rows
+ *   q_nope  bf16 [B, Sq, 128, 128] written (rounded to nearest, ties to even)
+ *   q_pe    bf16 [B, Sq, 128, 64]  written
+ * Numerics: bf16 products exact, fp32 accumulation; c_Q is kept in fp32 and
+ * enters the second product as hi + lo bf16 halves. Four kernels on `stream`;
+ * `workspace` (mla_query_project_workspace_size bytes, 256-byte aligned)
+ * holds the partial sums, c_Q and the unrounded q. Errors as for
+ * mla_decode_run. */
+typedef struct mla_query_args {
+  const void* hidden;         /* bf16 [B, Sq, 7168] */
+  const void* w_dq;           /* bf16 [1536, 7168] */
+  const void* w_uq;           /* bf16 [128, 192, 1536] */
+  const int32_t* seq_lens;    /* int32 [B], counting the new tokens */
+  void* q_nope;               /* bf16 [B, Sq, 128, 128], written */
+  void* q_pe;                 /* bf16 [B, Sq, 128, 64], written */
+  int32_t batch;              /* 1 <= B <= 1000000 */
+  int32_t q_tokens;           /* Sq: 1 or 2, <= max_q_tokens */
+  float rope_base;            /* <= 0 selects 10000 */
+} mla_query_args;
+
+int mla_query_project_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                                     size_t* bytes);
+
+int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* args, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* ---- Output projection -----------------------------------------------------
  *
  * y[t, :] = W_O x_t: the attention outputs of token t (the `out` of

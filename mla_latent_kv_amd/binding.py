@@ -67,6 +67,20 @@ class MlaAppendArgs(ctypes.Structure):
     ]
 
 
+class MlaQueryArgs(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_void_p),
+        ("w_dq", ctypes.c_void_p),
+        ("w_uq", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("q_nope", ctypes.c_void_p),
+        ("q_pe", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("q_tokens", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+    ]
+
+
 class MlaOprojArgs(ctypes.Structure):
     _fields_ = [
         ("x", ctypes.c_void_p),
@@ -108,6 +122,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_cache_append.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaAppendArgs),
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_cache_append.restype = ctypes.c_int
+    lib.mla_query_project_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_query_project_workspace_size.restype = ctypes.c_int
+    lib.mla_query_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaQueryArgs),
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_query_project.restype = ctypes.c_int
     lib.mla_output_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaOprojArgs), ctypes.c_void_p]
     lib.mla_output_project.restype = ctypes.c_int
     lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
@@ -264,6 +284,52 @@ def mla_cache_append(ctx, hidden, w_dkv, w_kr, kv_cache, block_table, seq_lens,
     return kv_cache
 
 
+def mla_query_project_workspace_size(ctx, batch: int, q_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mla_query_project_workspace_size(ctx, int(batch), int(q_tokens),
+                                                           ctypes.byref(n)),
+           "mla_query_project_workspace_size")
+    return n.value
+
+
+def mla_query_project(ctx, hidden, w_dq, w_uq, seq_lens, rope_base: float = 0.0,
+                      q_nope=None, q_pe=None, workspace=None, stream=None):
+    """Enqueue the query side: returns (q_nope [B, Sq, 128, 128], q_pe [B, Sq, 128, 64]),
+    both bf16, from hidden [B, Sq, 7168], w_dq [1536, 7168], w_uq [128, 192, 1536]."""
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _require(hidden, "hidden", b16, 3)
+    _require(w_dq, "w_dq", b16, 2)
+    _require(w_uq, "w_uq", b16, 3)
+    _require(seq_lens, "seq_lens", (torch.int32,), 1)
+    B, Sq = hidden.shape[0], hidden.shape[1]
+    if hidden.shape[2] != D_HIDDEN or tuple(seq_lens.shape) != (B,):
+        raise ValueError("hidden must be [B, Sq, 7168] and seq_lens [B]")
+    if tuple(w_dq.shape) != (1536, D_HIDDEN) or tuple(w_uq.shape) != (N_HEADS, D_NOPE + D_ROPE, 1536):
+        raise ValueError("w_dq / w_uq must be [1536, 7168] / [128, 192, 1536]")
+    if q_nope is None:
+        q_nope = torch.empty((B, Sq, N_HEADS, D_NOPE), dtype=torch.bfloat16, device=hidden.device)
+    if q_pe is None:
+        q_pe = torch.empty((B, Sq, N_HEADS, D_ROPE), dtype=torch.bfloat16, device=hidden.device)
+    _require(q_nope, "q_nope", b16, 4)
+    _require(q_pe, "q_pe", b16, 4)
+    if tuple(q_nope.shape) != (B, Sq, N_HEADS, D_NOPE) or tuple(q_pe.shape) != (B, Sq, N_HEADS, D_ROPE):
+        raise ValueError("q_nope / q_pe shapes must be [B, Sq, 128, 128] / [B, Sq, 128, 64]")
+    need = mla_query_project_workspace_size(ctx, B, Sq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
+    args = MlaQueryArgs(hidden.data_ptr(), w_dq.data_ptr(), w_uq.data_ptr(), seq_lens.data_ptr(),
+                        q_nope.data_ptr(), q_pe.data_ptr(), B, Sq, float(rope_base))
+    _check(load_library().mla_query_project(ctx, ctypes.byref(args), workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(),
+                                            ctypes.c_void_p(s.cuda_stream)),
+           "mla_query_project")
+    return q_nope, q_pe
+
+
 def mla_output_project(ctx, x, w_o, y=None, stream=None):
     """Enqueue y = W_O x: x fp32 [T, 16384] (or mla_decode_run's out [B, Sq,
     128, 128], viewed flat), w_o bf16 [7168, 16384]; returns y fp32 [T, 7168]."""
@@ -303,6 +369,10 @@ class MLADecoder:
     def append(self, *args, **kw):
         """Forwards to mla_cache_append (the new tokens' cache rows)."""
         return mla_cache_append(self.ctx, *args, **kw)
+
+    def query_project(self, *args, **kw):
+        """Forwards to mla_query_project (q_nope, q_pe of the new tokens)."""
+        return mla_query_project(self.ctx, *args, **kw)
 
     def output_project(self, *args, **kw):
         """Forwards to mla_output_project (y = W_O x)."""

@@ -206,6 +206,43 @@ int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* a, void* 
   return status;
 }
 
+int mla_query_project_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                                     size_t* bytes) {
+  if (!ctx || !bytes || batch < 1 || batch > mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
+  if (q_tokens < 1 || q_tokens > ctx->cfg.max_q_tokens) return MLA_ERR_INVALID_ARG;
+  *bytes = mla::qproj_workspace_bytes(batch * q_tokens);
+  return MLA_OK;
+}
+
+int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* a, void* workspace,
+                      size_t workspace_bytes, void* stream_handle) {
+  if (!ctx || !a || !a->hidden || !a->w_dq || !a->w_uq || !a->seq_lens || !a->q_nope || !a->q_pe)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->batch > mla::kMaxBatch || a->q_tokens < 1 ||
+      a->q_tokens > ctx->cfg.max_q_tokens)
+    return MLA_ERR_INVALID_ARG;
+  if (!(a->rope_base == a->rope_base)) return MLA_ERR_INVALID_ARG;   // NaN
+  if (!aligned16(a->hidden) || !aligned16(a->w_dq) || !aligned16(a->w_uq) ||
+      !aligned16(a->seq_lens) || !aligned16(a->q_nope) || !aligned16(a->q_pe))
+    return MLA_ERR_MISALIGNED;
+  const size_t need = mla::qproj_workspace_bytes(a->batch * a->q_tokens);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  const double base = a->rope_base > 0.f ? (double)a->rope_base : 10000.0;
+  const int status =
+      mla::launch_qproj((const uint16_t*)a->hidden, (const uint16_t*)a->w_dq,
+                        (const uint16_t*)a->w_uq, a->seq_lens, (uint16_t*)a->q_nope,
+                        (uint16_t*)a->q_pe, a->batch, a->q_tokens, base, (float*)workspace,
+                        stream) == hipSuccess
+          ? MLA_OK
+          : MLA_ERR_HIP;
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
+}
+
 int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* a, void* stream_handle) {
   if (!ctx || !a || !a->x || !a->w_o || !a->y) return MLA_ERR_INVALID_ARG;
   if (a->rows < 1 || a->rows > 2 * mla::kMaxBatch) return MLA_ERR_INVALID_ARG;

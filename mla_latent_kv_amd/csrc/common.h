@@ -119,6 +119,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 // [7168][16384], y fp32 [rows][7168]
 hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, hipStream_t stream);
 
+// query side (four launches): q_nope / q_pe of the new tokens from h
+size_t qproj_workspace_bytes(int rows);
+hipError_t launch_qproj(const uint16_t* hidden, const uint16_t* w_dq, const uint16_t* w_uq,
+                        const int32_t* seq_lens, uint16_t* q_nope, uint16_t* q_pe, int batch,
+                        int q_tokens, double rope_base, float* ws, hipStream_t stream);
+
 size_t append_workspace_bytes(int rows);
 hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_dkv, const uint16_t* w_kr,
                          uint16_t* cache, const int32_t* block_table, const int32_t* seq_lens,

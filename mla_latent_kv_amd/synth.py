@@ -166,3 +166,16 @@ def make_oproj_inputs(rows: int, seed: int, d_in: int = 128 * 128, d_model: int 
     r_x, r_w = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(2))
     return {"x": r_x.standard_normal((rows, d_in), dtype=np.float32),
             "w_o": _normal_bits(r_w, (d_model, d_in), std=1.0 / np.sqrt(d_in))}
+
+
+def make_query_inputs(batch: int, q_tokens: int, seed: int, d_hidden: int = D_HIDDEN,
+                      d_q: int = 1536, heads: int = 128, d_qk: int = 192) -> dict:
+    """Inputs of the query side as bf16 bits: hidden [B, Sq, d_hidden] ~ N(0, 1),
+    w_dq [d_q, d_hidden] ~ N(0, 1/d_hidden), w_uq [heads, d_qk, d_q] ~ N(0, 1/d_q)
+    (unit-variance c_Q and queries, like the decode workloads' q)."""
+    r_h, r_d, r_u = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3))
+    return {
+        "hidden": _normal_bits(r_h, (batch, q_tokens, d_hidden)),
+        "w_dq": _normal_bits(r_d, (d_q, d_hidden), std=1.0 / np.sqrt(d_hidden)),
+        "w_uq": _normal_bits(r_u, (heads, d_qk, d_q), std=1.0 / np.sqrt(d_q)),
+    }
