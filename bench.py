@@ -38,6 +38,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 APPEND_WEIGHT_BYTES = (512 + 64) * 7168 * 2   # W_DKV and W_KR, bf16
 OPROJ_WEIGHT_BYTES = 7168 * 16384 * 2         # W_O, bf16
+QPROJ_WEIGHT_BYTES = (1536 * 7168 + 128 * 192 * 1536) * 2   # W_DQ and W_UQ, bf16
 
 # HBM traffic of one attention launch from two rocprofv3 --pmc runs of this
 # script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
@@ -243,6 +244,61 @@ def time_output_project(lib, dec, B, Sq, stream, args) -> dict:
     return out
 
 
+def time_query_project(lib, dec, d, B, Sq, stream, args) -> dict:
+    """The query side for the batch's new tokens (W_DQ and W_UQ, 97.5 MB of
+    weights), HIP events around the calls; weight copies alternate past the
+    Infinity Cache."""
+    import torch
+    from mla_latent_kv_amd import binding, synth
+    rows = B * Sq
+    inp = synth.make_query_inputs(B, Sq, seed=3000)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    hid = bf16(inp["hidden"])
+    w0 = (bf16(inp["w_dq"]), bf16(inp["w_uq"]))
+    n_w = max(2, math.ceil(MALL_BYTES / QPROJ_WEIGHT_BYTES) + 1)
+    ws = [w0] + [(w0[0].clone(), w0[1].clone()) for _ in range(n_w - 1)]
+    qn = torch.empty((B, Sq, 128, 128), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((B, Sq, 128, 64), dtype=torch.bfloat16, device="cuda")
+    need = binding.mla_query_project_workspace_size(dec.ctx, B, Sq)
+    wsp = torch.empty(need, dtype=torch.uint8, device="cuda")
+    cargs = [binding.MlaQueryArgs(hid.data_ptr(), a.data_ptr(), b.data_ptr(), d["seq_lens"].data_ptr(),
+                                  qn.data_ptr(), qp.data_ptr(), B, Sq, 0.0) for a, b in ws]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(i):
+        rc = lib.mla_query_project(dec.ctx, ctypes.byref(cargs[i % n_w]), ctypes.c_void_p(wsp.data_ptr()),
+                                   need, sh)
+        if rc != 0:
+            raise RuntimeError(binding.mla_decode_status_string(rc))
+
+    for i in range(max(2, args.warmup // 2)):
+        call(i)
+    torch.cuda.synchronize()
+    n = max(4, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    nbytes = QPROJ_WEIGHT_BYTES + rows * 7168 * 2 + rows * 128 * 192 * 2
+    out = {"us_per_call": us, "tokens": rows, "rotating_weight_sets": n_w, "calls": n,
+           "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+           "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "launches": 4}
+    if not args.no_cpu:
+        from oracle import mla_oracle as orc
+        reps, t0 = 0, time.perf_counter()
+        while reps < 2 or time.perf_counter() - t0 < 1.0:
+            orc.query_batch(inp["hidden"], inp["w_dq"], inp["w_uq"], d["seq_lens"].cpu().numpy(), Sq)
+            reps += 1
+        out["cpu_oracle_us_per_call"] = (time.perf_counter() - t0) / reps * 1e6
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +309,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-append", action="store_true",
-                    help="skip the timings of the cache-append producer and the output projection")
+                    help="skip the timings of the cache-append producer, the query side and the "
+                         "output projection")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -386,6 +443,7 @@ def main() -> int:
     }
     if not args.no_append:
         result["cache_append"] = time_cache_append(lib, dec, d, B, Sq, stream, args)
+        result["query_project"] = time_query_project(lib, dec, d, B, Sq, stream, args)
         result["output_project"] = time_output_project(lib, dec, B, Sq, stream, args)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0])
