@@ -137,6 +137,29 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* ar
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]);
 
+/* ---- Packed weights of the projections -----------------------------------
+ *
+ * The projections below (cache append, query side, output projection) are
+ * weight streams: for a decode batch every weight byte is used by only a few
+ * dozen tokens, so they are bound by reading the weights from HBM. They take
+ * their weights in a packed layout, made once per weight (at load time) by
+ * mla_pack_weight from the row-major matrix W [n][k] (bf16):
+ *   the 1 KB block of column tile ct (rows 32 ct .. 32 ct + 31 of W) and
+ *   k-step ks (columns 16 ks .. 16 ks + 15) sits at byte (ks * n/32 + ct) *
+ *   1024; within it, 16-byte lane piece l (l = 0..63) holds
+ *   W[32 ct + l % 32][16 ks + 8 (l / 32) .. 16 ks + 8 (l / 32) + 7].
+ * That is the operand fragment order of the 32x32x16 bf16 matrix
+ * instructions, so every load of the stream is one contiguous 1 KB. The
+ * packed matrix has the same size, n * k * 2 bytes; it is a permutation of
+ * the bytes (packing is exact).
+ *
+ * `w` and `packed`: device memory, borrowed, 16-byte aligned, not
+ * overlapping; n % 32 == 0, k % 16 == 0, n * k <= 2^33. One kernel on
+ * `stream`, no allocation, no synchronisation. Errors: MLA_ERR_INVALID_ARG
+ * (NULL, shape, overlap), MLA_ERR_MISALIGNED, MLA_ERR_HIP. */
+int mla_pack_weight(const mla_decode_ctx* ctx, const void* w, void* packed, int32_t n, int32_t k,
+                    void* stream);
+
 /* ---- Cache-append producer ------------------------------------------------
  *
  * Writes the cache rows of a decode step's new tokens: per token the short
@@ -153,10 +176,10 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* ar
  * embedding without a formula; this is its own definition, no length
  * scaling). Angles are formed in fp64.
  *
- * Layouts (row-major, device memory, borrowed):
- *   hidden   bf16 [B, Sq, 7168]
- *   w_dkv    bf16 [512, 7168]
- *   w_kr     bf16 [64, 7168]
+ * Layouts (device memory, borrowed, 16-byte aligned):
+ *   hidden   bf16 [B, Sq, 7168] row-major
+ *   w_kv     the stacked weight [W_DKV; W_KR] (576 x 7168: rows 0..511 are
+ *            W_DKV, rows 512..575 W_KR) packed by mla_pack_weight
  *   kv_cache bf16 [num_blocks, 64, 576]: only the new tokens' rows are written;
  *            a token whose position or block id is out of range is skipped
  * Numerics: bf16 products exact, fp32 accumulation, one rounding to bf16 of
@@ -167,8 +190,7 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* ar
  * for mla_decode_run. */
 typedef struct mla_append_args {
   const void* hidden;          /* bf16 [B, Sq, 7168] */
-  const void* w_dkv;           /* bf16 [512, 7168] */
-  const void* w_kr;            /* bf16 [64, 7168] */
+  const void* w_kv;            /* packed [W_DKV; W_KR], 576 x 7168 */
   void* kv_cache;              /* bf16 [num_blocks, 64, 576]; rows written */
   const int32_t* block_table;  /* int32 [B, max_blocks_per_seq] */
   const int32_t* seq_lens;     /* int32 [B], counting the new tokens */
@@ -199,22 +221,22 @@ int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* args, voi
  * with pos = seq_lens[b] - q_tokens + i and the RoPE of mla_cache_append. The
  * outputs are exactly mla_decode_run's q_nope and q_pe inputs.
  *
- * Layouts (row-major, device memory, borrowed; 16-byte aligned):
- *   hidden  bf16 [B, Sq, 7168]
- *   w_dq    bf16 [1536, 7168]
- *   w_uq    bf16 [128, 192, 1536]  per head: 128 non-positional rows, then 64
- *                                  position rows
+ * Layouts (device memory, borrowed, 16-byte aligned):
+ *   hidden  bf16 [B, Sq, 7168] row-major
+ *   w_dq    W_DQ (1536 x 7168) packed by mla_pack_weight
+ *   w_uq    W_UQ (24576 x 1536: head h's 192 rows at 192 h, 128
+ *           non-positional rows, then 64 position rows) packed by
+ *           mla_pack_weight
  *   q_nope  bf16 [B, Sq, 128, 128] written (rounded to nearest, ties to even)
  *   q_pe    bf16 [B, Sq, 128, 64]  written
  * Numerics: bf16 products exact, fp32 accumulation; c_Q is kept in fp32 and
- * enters the second product as hi + lo bf16 halves. Four kernels on `stream`;
+ * enters the second product as hi + lo bf16 halves. Three kernels on `stream`;
  * `workspace` (mla_query_project_workspace_size bytes, 256-byte aligned)
- * holds the partial sums, c_Q and the unrounded q. Errors as for
- * mla_decode_run. */
+ * holds the partial sums and c_Q. Errors as for mla_decode_run. */
 typedef struct mla_query_args {
   const void* hidden;         /* bf16 [B, Sq, 7168] */
-  const void* w_dq;           /* bf16 [1536, 7168] */
-  const void* w_uq;           /* bf16 [128, 192, 1536] */
+  const void* w_dq;           /* packed W_DQ, 1536 x 7168 */
+  const void* w_uq;           /* packed W_UQ, 24576 x 1536 */
   const int32_t* seq_lens;    /* int32 [B], counting the new tokens */
   void* q_nope;               /* bf16 [B, Sq, 128, 128], written */
   void* q_pe;                 /* bf16 [B, Sq, 128, 64], written */
@@ -236,22 +258,28 @@ int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* args, voi
  * mapped back to the model width 7168 by one output projection matrix
  * ("DeepSeek-V3" page at ailearn.mscapital.top, MLA state flow).
  *
- * Layouts (row-major, device memory, borrowed; 16-byte aligned):
- *   x    fp32 [rows, 16384]      (mla_decode_run's out viewed as [B * Sq, 16384])
- *   w_o  bf16 [7168, 16384]
+ * Layouts (device memory, borrowed, 16-byte aligned):
+ *   x    fp32 [rows, 16384] row-major (mla_decode_run's out viewed as
+ *        [B * Sq, 16384])
+ *   w_o  W_O (7168 x 16384) packed by mla_pack_weight
  *   y    fp32 [rows, 7168]       written
  * Numerics: x enters the bf16 matrix cores as x = hi + lo (hi = bf16(x), lo =
- * bf16(x - hi), together within 2^-17 of x); products are accumulated in fp32.
- * One kernel on `stream`, no workspace, no allocation, no synchronisation.
- * Errors as for mla_decode_run. */
+ * bf16(x - hi), together within 2^-17 of x); products are accumulated in fp32
+ * and the four K-splits added in a fixed order. Three kernels on `stream`, no
+ * allocation, no synchronisation; `workspace` (the packed input and the
+ * partial sums, mla_output_project_workspace_size bytes, 256-byte aligned)
+ * must not be shared by overlapping calls. Errors as for mla_decode_run. */
 typedef struct mla_oproj_args {
   const float* x;    /* fp32 [rows, 16384] */
-  const void* w_o;   /* bf16 [7168, 16384] */
+  const void* w_o;   /* packed W_O, 7168 x 16384 */
   float* y;          /* fp32 [rows, 7168] */
-  int32_t rows;      /* tokens, >= 1 */
+  int32_t rows;      /* tokens, 1 <= rows <= 2000000 */
 } mla_oproj_args;
 
-int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* args, void* stream);
+int mla_output_project_workspace_size(const mla_decode_ctx* ctx, int32_t rows, size_t* bytes);
+
+int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* args, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Release a context (NULL is accepted). */
 void mla_decode_destroy(mla_decode_ctx* ctx);

@@ -54,8 +54,7 @@ class MlaDecodeArgs(ctypes.Structure):
 class MlaAppendArgs(ctypes.Structure):
     _fields_ = [
         ("hidden", ctypes.c_void_p),
-        ("w_dkv", ctypes.c_void_p),
-        ("w_kr", ctypes.c_void_p),
+        ("w_kv", ctypes.c_void_p),
         ("kv_cache", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p),
@@ -128,8 +127,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_query_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaQueryArgs),
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_query_project.restype = ctypes.c_int
-    lib.mla_output_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaOprojArgs), ctypes.c_void_p]
+    lib.mla_output_project_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_output_project_workspace_size.restype = ctypes.c_int
+    lib.mla_output_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaOprojArgs),
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_output_project.restype = ctypes.c_int
+    lib.mla_pack_weight.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p]
+    lib.mla_pack_weight.restype = ctypes.c_int
     lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
     lib.mla_decode_destroy.restype = None
     lib.mla_decode_status_string.argtypes = [ctypes.c_int]
@@ -233,6 +239,46 @@ def mla_decode_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_len
     return out
 
 
+def _workspace(workspace, need, device):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    return workspace
+
+
+def _require_packed(t, name, n, k):
+    """A weight packed by mla_pack_weight: a flat bf16 tensor of n * k elements."""
+    import torch
+    _require(t, name, (torch.bfloat16, torch.int16, torch.uint16), 1)
+    if t.numel() != n * k:
+        raise ValueError(f"{name} must be the packed {n} x {k} weight ({n * k} elements), "
+                         f"got {t.numel()}")
+
+
+def mla_pack_weight(ctx, w, packed=None, stream=None):
+    """Pack a row-major bf16 weight [n, k] (a 3-d tensor is viewed as [prod of
+    leading dims, k]) into the layout the projections stream (include/mla_decode.h,
+    mla_pack_weight). Returns a flat tensor of n * k elements, w's dtype."""
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    if isinstance(w, torch.Tensor) and w.dim() > 2:
+        w = w.reshape(-1, w.shape[-1])
+    _require(w, "w", b16, 2)
+    n, k = w.shape
+    if packed is None:
+        packed = torch.empty(n * k, dtype=w.dtype, device=w.device)
+    _require(packed, "packed", b16, 1)
+    if packed.numel() != n * k:
+        raise ValueError("packed must hold n * k elements")
+    s = stream if stream is not None else torch.cuda.current_stream(w.device)
+    _check(load_library().mla_pack_weight(ctx, w.data_ptr(), packed.data_ptr(), n, k,
+                                          ctypes.c_void_p(s.cuda_stream)),
+           "mla_pack_weight")
+    return packed
+
+
 def mla_cache_append_workspace_size(ctx, batch: int, q_tokens: int) -> int:
     n = ctypes.c_size_t()
     _check(load_library().mla_cache_append_workspace_size(ctx, int(batch), int(q_tokens),
@@ -241,40 +287,33 @@ def mla_cache_append_workspace_size(ctx, batch: int, q_tokens: int) -> int:
     return n.value
 
 
-def mla_cache_append(ctx, hidden, w_dkv, w_kr, kv_cache, block_table, seq_lens,
+def mla_cache_append(ctx, hidden, w_kv, kv_cache, block_table, seq_lens,
                      rope_base: float = 0.0, workspace=None, stream=None):
     """Enqueue the cache-append producer: writes the new tokens' rows
     [W_DKV h | RoPE(W_KR h, pos)] (bf16) into ``kv_cache`` in place and returns it.
 
-    hidden [B, Sq, 7168], w_dkv [512, 7168], w_kr [64, 7168], kv_cache
-    [num_blocks, 64, 576] (bf16 or 16-bit integer views of the bits),
-    block_table int32 [B, max_blocks_per_seq], seq_lens int32 [B] counting the
-    new tokens. ``rope_base`` <= 0 selects 10000.
+    hidden [B, Sq, 7168]; w_kv the stacked [W_DKV; W_KR] (576 x 7168) packed by
+    mla_pack_weight; kv_cache [num_blocks, 64, 576] (bf16 or 16-bit integer
+    views of the bits), block_table int32 [B, max_blocks_per_seq], seq_lens
+    int32 [B] counting the new tokens. ``rope_base`` <= 0 selects 10000.
     """
     import torch
     b16 = (torch.bfloat16, torch.int16, torch.uint16)
     _require(hidden, "hidden", b16, 3)
-    _require(w_dkv, "w_dkv", b16, 2)
-    _require(w_kr, "w_kr", b16, 2)
+    _require_packed(w_kv, "w_kv", D_LATENT + D_ROPE, D_HIDDEN)
     _require(kv_cache, "kv_cache", b16, 3)
     _require(block_table, "block_table", (torch.int32,), 2)
     _require(seq_lens, "seq_lens", (torch.int32,), 1)
     B, Sq = hidden.shape[0], hidden.shape[1]
     if hidden.shape[2] != D_HIDDEN:
         raise ValueError("hidden must be [B, Sq, 7168]")
-    if tuple(w_dkv.shape) != (D_LATENT, D_HIDDEN) or tuple(w_kr.shape) != (D_ROPE, D_HIDDEN):
-        raise ValueError("w_dkv / w_kr must be [512, 7168] / [64, 7168]")
     if tuple(kv_cache.shape[1:]) != (BLOCK, D_LATENT + D_ROPE):
         raise ValueError("kv_cache must be [num_blocks, 64, 576]")
     if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
         raise ValueError("block_table / seq_lens batch mismatch")
-    need = mla_cache_append_workspace_size(ctx, B, Sq)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    workspace = _workspace(workspace, mla_cache_append_workspace_size(ctx, B, Sq), hidden.device)
     s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
-    args = MlaAppendArgs(hidden.data_ptr(), w_dkv.data_ptr(), w_kr.data_ptr(), kv_cache.data_ptr(),
+    args = MlaAppendArgs(hidden.data_ptr(), w_kv.data_ptr(), kv_cache.data_ptr(),
                          block_table.data_ptr(), seq_lens.data_ptr(), kv_cache.shape[0], B, Sq,
                          block_table.shape[1], float(rope_base))
     _check(load_library().mla_cache_append(ctx, ctypes.byref(args), workspace.data_ptr(),
@@ -295,18 +334,17 @@ def mla_query_project_workspace_size(ctx, batch: int, q_tokens: int) -> int:
 def mla_query_project(ctx, hidden, w_dq, w_uq, seq_lens, rope_base: float = 0.0,
                       q_nope=None, q_pe=None, workspace=None, stream=None):
     """Enqueue the query side: returns (q_nope [B, Sq, 128, 128], q_pe [B, Sq, 128, 64]),
-    both bf16, from hidden [B, Sq, 7168], w_dq [1536, 7168], w_uq [128, 192, 1536]."""
+    both bf16, from hidden [B, Sq, 7168] and the packed W_DQ (1536 x 7168) and
+    W_UQ (128 x 192 rows x 1536) of mla_pack_weight."""
     import torch
     b16 = (torch.bfloat16, torch.int16, torch.uint16)
     _require(hidden, "hidden", b16, 3)
-    _require(w_dq, "w_dq", b16, 2)
-    _require(w_uq, "w_uq", b16, 3)
+    _require_packed(w_dq, "w_dq", 1536, D_HIDDEN)
+    _require_packed(w_uq, "w_uq", N_HEADS * (D_NOPE + D_ROPE), 1536)
     _require(seq_lens, "seq_lens", (torch.int32,), 1)
     B, Sq = hidden.shape[0], hidden.shape[1]
     if hidden.shape[2] != D_HIDDEN or tuple(seq_lens.shape) != (B,):
         raise ValueError("hidden must be [B, Sq, 7168] and seq_lens [B]")
-    if tuple(w_dq.shape) != (1536, D_HIDDEN) or tuple(w_uq.shape) != (N_HEADS, D_NOPE + D_ROPE, 1536):
-        raise ValueError("w_dq / w_uq must be [1536, 7168] / [128, 192, 1536]")
     if q_nope is None:
         q_nope = torch.empty((B, Sq, N_HEADS, D_NOPE), dtype=torch.bfloat16, device=hidden.device)
     if q_pe is None:
@@ -315,11 +353,7 @@ def mla_query_project(ctx, hidden, w_dq, w_uq, seq_lens, rope_base: float = 0.0,
     _require(q_pe, "q_pe", b16, 4)
     if tuple(q_nope.shape) != (B, Sq, N_HEADS, D_NOPE) or tuple(q_pe.shape) != (B, Sq, N_HEADS, D_ROPE):
         raise ValueError("q_nope / q_pe shapes must be [B, Sq, 128, 128] / [B, Sq, 128, 64]")
-    need = mla_query_project_workspace_size(ctx, B, Sq)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {need}")
+    workspace = _workspace(workspace, mla_query_project_workspace_size(ctx, B, Sq), hidden.device)
     s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
     args = MlaQueryArgs(hidden.data_ptr(), w_dq.data_ptr(), w_uq.data_ptr(), seq_lens.data_ptr(),
                         q_nope.data_ptr(), q_pe.data_ptr(), B, Sq, float(rope_base))
@@ -330,24 +364,35 @@ def mla_query_project(ctx, hidden, w_dq, w_uq, seq_lens, rope_base: float = 0.0,
     return q_nope, q_pe
 
 
-def mla_output_project(ctx, x, w_o, y=None, stream=None):
+def mla_output_project_workspace_size(ctx, rows: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mla_output_project_workspace_size(ctx, int(rows), ctypes.byref(n)),
+           "mla_output_project_workspace_size")
+    return n.value
+
+
+def mla_output_project(ctx, x, w_o, y=None, workspace=None, stream=None):
     """Enqueue y = W_O x: x fp32 [T, 16384] (or mla_decode_run's out [B, Sq,
-    128, 128], viewed flat), w_o bf16 [7168, 16384]; returns y fp32 [T, 7168]."""
+    128, 128], viewed flat), w_o the packed W_O (7168 x 16384) of
+    mla_pack_weight; returns y fp32 [T, 7168]."""
     import torch
     if x.dim() == 4:
         x = x.reshape(-1, N_HEADS * D_V)
     _require(x, "x", (torch.float32,), 2)
-    _require(w_o, "w_o", (torch.bfloat16, torch.int16, torch.uint16), 2)
-    if x.shape[1] != N_HEADS * D_V or tuple(w_o.shape) != (D_HIDDEN, N_HEADS * D_V):
-        raise ValueError("x must be [T, 16384] and w_o [7168, 16384]")
+    _require_packed(w_o, "w_o", D_HIDDEN, N_HEADS * D_V)
+    if x.shape[1] != N_HEADS * D_V:
+        raise ValueError("x must be [T, 16384]")
     if y is None:
         y = torch.empty((x.shape[0], D_HIDDEN), dtype=torch.float32, device=x.device)
     _require(y, "y", (torch.float32,), 2)
     if tuple(y.shape) != (x.shape[0], D_HIDDEN):
         raise ValueError("y must be [T, 7168] fp32")
+    workspace = _workspace(workspace, mla_output_project_workspace_size(ctx, x.shape[0]), x.device)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     args = MlaOprojArgs(x.data_ptr(), w_o.data_ptr(), y.data_ptr(), x.shape[0])
-    _check(load_library().mla_output_project(ctx, ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)),
+    _check(load_library().mla_output_project(ctx, ctypes.byref(args), workspace.data_ptr(),
+                                             workspace.numel() * workspace.element_size(),
+                                             ctypes.c_void_p(s.cuda_stream)),
            "mla_output_project")
     return y
 
@@ -365,6 +410,10 @@ class MLADecoder:
 
     def __call__(self, *args, **kw):
         return mla_decode_run(self.ctx, *args, **kw)
+
+    def pack(self, w, **kw):
+        """Forwards to mla_pack_weight (a weight in the projections' packed layout)."""
+        return mla_pack_weight(self.ctx, w, **kw)
 
     def append(self, *args, **kw):
         """Forwards to mla_cache_append (the new tokens' cache rows)."""

@@ -178,14 +178,13 @@ int mla_cache_append_workspace_size(const mla_decode_ctx* ctx, int32_t batch, in
 int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* a, void* workspace,
                      size_t workspace_bytes, void* stream_handle) {
   if (!ctx || !a) return MLA_ERR_INVALID_ARG;
-  if (!a->hidden || !a->w_dkv || !a->w_kr || !a->kv_cache || !a->block_table || !a->seq_lens)
-    return MLA_ERR_INVALID_ARG;
+  if (!a->hidden || !a->w_kv || !a->kv_cache || !a->block_table || !a->seq_lens) return MLA_ERR_INVALID_ARG;
   if (a->batch < 1 || a->batch > mla::kMaxBatch || a->q_tokens < 1 ||
       a->q_tokens > ctx->cfg.max_q_tokens || a->num_blocks < 1 || a->max_blocks_per_seq < 1)
     return MLA_ERR_INVALID_ARG;
   if (!(a->rope_base == a->rope_base)) return MLA_ERR_INVALID_ARG;   // NaN
-  if (!aligned16(a->hidden) || !aligned16(a->w_dkv) || !aligned16(a->w_kr) ||
-      !aligned16(a->kv_cache) || !aligned16(a->block_table) || !aligned16(a->seq_lens))
+  if (!aligned16(a->hidden) || !aligned16(a->w_kv) || !aligned16(a->kv_cache) ||
+      !aligned16(a->block_table) || !aligned16(a->seq_lens))
     return MLA_ERR_MISALIGNED;
   const size_t need = mla::append_workspace_bytes(a->batch * a->q_tokens);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
@@ -196,10 +195,9 @@ int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* a, void* 
   if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
   const double base = a->rope_base > 0.f ? (double)a->rope_base : 10000.0;
   const int status =
-      mla::launch_append((const uint16_t*)a->hidden, (const uint16_t*)a->w_dkv,
-                         (const uint16_t*)a->w_kr, (uint16_t*)a->kv_cache, a->block_table,
-                         a->seq_lens, a->num_blocks, a->max_blocks_per_seq, a->batch,
-                         a->q_tokens, base, (float*)workspace, stream) == hipSuccess
+      mla::launch_append((const uint16_t*)a->hidden, (const uint16_t*)a->w_kv, (uint16_t*)a->kv_cache,
+                         a->block_table, a->seq_lens, a->num_blocks, a->max_blocks_per_seq, a->batch,
+                         a->q_tokens, base, workspace, stream) == hipSuccess
           ? MLA_OK
           : MLA_ERR_HIP;
   if (prev != ctx->device) (void)hipSetDevice(prev);
@@ -235,25 +233,52 @@ int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* a, void* 
   const int status =
       mla::launch_qproj((const uint16_t*)a->hidden, (const uint16_t*)a->w_dq,
                         (const uint16_t*)a->w_uq, a->seq_lens, (uint16_t*)a->q_nope,
-                        (uint16_t*)a->q_pe, a->batch, a->q_tokens, base, (float*)workspace,
-                        stream) == hipSuccess
+                        (uint16_t*)a->q_pe, a->batch, a->q_tokens, base, workspace, stream) == hipSuccess
           ? MLA_OK
           : MLA_ERR_HIP;
   if (prev != ctx->device) (void)hipSetDevice(prev);
   return status;
 }
 
-int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* a, void* stream_handle) {
+int mla_output_project_workspace_size(const mla_decode_ctx* ctx, int32_t rows, size_t* bytes) {
+  if (!ctx || !bytes || rows < 1 || rows > 2 * mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
+  *bytes = mla::oproj_workspace_bytes(rows);
+  return MLA_OK;
+}
+
+int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* a, void* workspace,
+                       size_t workspace_bytes, void* stream_handle) {
   if (!ctx || !a || !a->x || !a->w_o || !a->y) return MLA_ERR_INVALID_ARG;
   if (a->rows < 1 || a->rows > 2 * mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
   if (!aligned16(a->x) || !aligned16(a->w_o) || !aligned16(a->y)) return MLA_ERR_MISALIGNED;
+  const size_t need = mla::oproj_workspace_bytes(a->rows);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_handle;
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
   if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
-  const int status = mla::launch_oproj(a->x, (const uint16_t*)a->w_o, a->y, a->rows, stream) == hipSuccess
-                         ? MLA_OK
-                         : MLA_ERR_HIP;
+  const int status =
+      mla::launch_oproj(a->x, (const uint16_t*)a->w_o, a->y, a->rows, workspace, stream) == hipSuccess
+          ? MLA_OK
+          : MLA_ERR_HIP;
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
+}
+
+int mla_pack_weight(const mla_decode_ctx* ctx, const void* w, void* packed, int32_t n, int32_t k,
+                    void* stream_handle) {
+  if (!ctx || !w || !packed) return MLA_ERR_INVALID_ARG;
+  if (n < 32 || k < 16 || n % 32 || k % 16 || (long long)n * k > (1LL << 33)) return MLA_ERR_INVALID_ARG;
+  const uintptr_t wb = (uintptr_t)w, pb = (uintptr_t)packed, nb = (uintptr_t)n * (uintptr_t)k * 2u;
+  if (wb < pb + nb && pb < wb + nb) return MLA_ERR_INVALID_ARG;   // overlapping buffers
+  if (!aligned16(w) || !aligned16(packed)) return MLA_ERR_MISALIGNED;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  const int status =
+      mla::launch_pack_weight((const uint16_t*)w, (uint16_t*)packed, n, k, stream) == hipSuccess ? MLA_OK
+                                                                                                 : MLA_ERR_HIP;
   if (prev != ctx->device) (void)hipSetDevice(prev);
   return status;
 }

@@ -19,7 +19,6 @@ constexpr int kRow = kDLat + kDRope;    // 576 cached elements per token
 constexpr int kRowBytes = kRow * 2;     // 1152
 constexpr int kBlock = 64;              // tokens per cache block
 constexpr int kDHidden = 7168;          // model width, input of the cache-append producer
-constexpr int kAppKSplit = 16;          // K-chunks of the cache-append product
 
 // Work decomposition of the attention pass.
 constexpr int kTileTok = 32;            // cached tokens per LDS tile
@@ -112,24 +111,28 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
-// cache-append producer (two launches): fp32 partials of W h per K-chunk in
-// `part` (append_workspace_bytes), then the sums, RoPE, bf16 rounding and the
-// writes of the new tokens' cache rows
-// output projection y = W_O x (one launch): x fp32 [rows][16384], W_O bf16
-// [7168][16384], y fp32 [rows][7168]
-hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, hipStream_t stream);
+// Weight-stream products (wstream.h); every weight in the packed layout that
+// launch_pack_weight writes (n % 32 == 0, k % 16 == 0, n * k * 2 bytes).
+hipError_t launch_pack_weight(const uint16_t* w, uint16_t* packed, int n, int k, hipStream_t stream);
+
+// output projection y = W_O x (three launches): x fp32 [rows][16384], W_O
+// packed [7168][16384], y fp32 [rows][7168]
+size_t oproj_workspace_bytes(int rows);
+hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, void* ws, hipStream_t stream);
 
 // query side (four launches): q_nope / q_pe of the new tokens from h
 size_t qproj_workspace_bytes(int rows);
 hipError_t launch_qproj(const uint16_t* hidden, const uint16_t* w_dq, const uint16_t* w_uq,
                         const int32_t* seq_lens, uint16_t* q_nope, uint16_t* q_pe, int batch,
-                        int q_tokens, double rope_base, float* ws, hipStream_t stream);
+                        int q_tokens, double rope_base, void* ws, hipStream_t stream);
 
+// cache-append producer (three launches): the new tokens' cache rows from h
+// and the packed stacked weight [W_DKV; W_KR] ([576][7168])
 size_t append_workspace_bytes(int rows);
-hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_dkv, const uint16_t* w_kr,
-                         uint16_t* cache, const int32_t* block_table, const int32_t* seq_lens,
-                         long long num_blocks, int max_blocks_per_seq, int batch, int q_tokens,
-                         double rope_base, float* part, hipStream_t stream);
+hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_kv, uint16_t* cache,
+                         const int32_t* block_table, const int32_t* seq_lens, long long num_blocks,
+                         int max_blocks_per_seq, int batch, int q_tokens, double rope_base, void* ws,
+                         hipStream_t stream);
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const SeqInfo* seqinfo,
                         const uint16_t* w_uv, float* out, int batch, int q_tokens,
                         hipStream_t stream);

@@ -4,42 +4,35 @@
 // output projection matrix back to the model width ("DeepSeek-V3" page,
 // ailearn.mscapital.top, MLA state flow).
 //
-// A weight stream: for a decode batch (a few dozen tokens) every W_O byte is
-// used by only those tokens, so the bound is HBM (235 MB per call). One
-// launch of the weight-stream product (wstream.h), no partial sums in memory:
-// * workgroup = 32 output columns over the whole K = 16384; its 1 MB weight
-//   slice crosses HBM once. 224 workgroups.
-// * its 4 wavefronts split K (4096 each); each streams its weight and input
-//   tiles (chunks of 64 k: 4 KB of W_O rows, 8 KB of inputs) through its own
-//   3-stage LDS ring with direct-to-LDS fetches laid out so that every 1 KB
-//   fetch covers 8 whole cache lines (fragments loaded straight from global
-//   memory would touch 32 rows per instruction and starve the load path).
-//   Two chunks in flight per wavefront (≈ 96 KB per workgroup) cover HBM
-//   latency; the waits are explicit and no barrier is needed in the loop.
-// * D[n, t] = sum_k W[n][k] x[t][k] on 32x32x16 bf16 MFMA: both operands are
-//   row-major with k contiguous, so each fragment is one contiguous load.
-//   The fp32 input is split as x = hi + lo with hi = bf16(x) and
-//   lo = bf16(x - hi) (together within 2^-17 of x) and both halves are
-//   multiplied (two MFMAs per k-step); the matrix cores have ample slack
-//   against the weight stream.
-// * the 4 wavefront tiles are summed in LDS in a fixed order and stored as
-//   fp32. No atomics: results are deterministic.
-// More than 32 tokens loop over row tiles (each extra 32 tokens re-streams
-// the slice).
+// A weight stream (wstream.h): for a decode batch (a few dozen tokens) every
+// W_O byte is used by only those tokens, so the bound is HBM (235 MB per
+// call). Three launches on the caller's stream:
+//  1. x (fp32 rows) -> the packed input layout (2 MB for 32 tokens);
+//  2. the stream: 56 column blocks of 128 x 4 K-splits = 224 workgroups, each
+//     wavefront 64 k-steps (a quarter of its split); W_O in the packed weight
+//     layout, read once;
+//  3. the 4 splits' partial sums added in split order -> y.
 #include "wstream.h"
 
 namespace mla {
 
 namespace {
 constexpr int kOpK = kHeads * kDV;   // 16384
-static_assert(kDHidden % 32 == 0, "whole column tiles");
+using OprojPlan = ws::Plan<true, kDHidden, kOpK, 4, 4, 4>;
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 }  // namespace
 
-hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, hipStream_t stream) {
-  hipLaunchKernelGGL((ws::wstream_kernel<true, kOpK / 4>), dim3(kDHidden / 32, 1), dim3(ws::kThreads), 0,
-                     stream, (const void*)x, (long long)kOpK, w_o, (long long)kOpK, y,
-                     (long long)kDHidden, 0LL, rows);
-  return hipGetLastError();
+size_t oproj_workspace_bytes(int rows) {
+  return round256(OprojPlan::packed_x_bytes(rows)) + round256(OprojPlan::part_bytes(rows));
+}
+
+hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, void* ws, hipStream_t stream) {
+  char* xp = (char*)ws;
+  float* part = (float*)(xp + round256(OprojPlan::packed_x_bytes(rows)));
+  const hipError_t e = OprojPlan::pack_x(x, xp, rows, stream);
+  if (e != hipSuccess) return e;
+  return OprojPlan::run(xp, w_o, part, rows, ws::StoreF32{y, kDHidden}, stream);
 }
 
 }  // namespace mla

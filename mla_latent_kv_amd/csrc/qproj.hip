@@ -10,15 +10,17 @@
 // rotated like the shared position key ("DeepSeek-V3" article at m.lsln.cn,
 // section 2.3).
 //
-// Four launches on the caller's stream, all deterministic:
-//  1. split-K weight stream h -> c_Q partials (wstream.h; 48 column tiles x 7
-//     K-splits = 336 workgroups, W_DQ read once);
-//  2. the 7 partials summed in a fixed order -> c_Q (fp32);
-//  3. weight stream c_Q -> q (768 column tiles, W_UQ read once; c_Q enters
-//     as fp32 hi + lo);
-//  4. epilogue: per (token, head, column pair) the non-positional pairs are
-//     rounded to bf16 and the position pairs rotated (fp64 angles) and
-//     rounded (nearest, ties to even).
+// Three launches on the caller's stream (weight-stream products, wstream.h),
+// all deterministic:
+//  1. stream W_DQ: 48 column tiles x 16 K-splits = 768 workgroups, each
+//     wavefront with all its 7 k-steps in flight at once (h read from its
+//     rows), partial sums per split;
+//  2. the splits added in split order; c_Q (fp32) is written straight into
+//     the packed input layout of the second product;
+//  3. stream W_UQ: 256 column blocks of 96, one split (each wavefront 24
+//     k-steps); c_Q enters as fp32 hi + lo. Its epilogue finishes the heads:
+//     non-positional columns rounded to bf16, position pairs rotated (fp64
+//     angles) and rounded (nearest, ties to even).
 #include "wstream.h"
 
 namespace mla {
@@ -26,12 +28,13 @@ namespace mla {
 namespace {
 
 constexpr int kQRank = 1536;
-constexpr int kQRow = kDNope + kDRope;            // 192 rows of W_UQ per head
-constexpr int kQUp = kHeads * kQRow;              // 24576
-constexpr int kQDownSplit = 7;                    // K-splits of the first product
-constexpr int kQDownPerWave = kDHidden / kQDownSplit / 4;   // 256
-static_assert(kDHidden % (kQDownSplit * 4 * ws::kChunk) == 0, "whole chunks per split");
-static_assert(kQRank % (4 * ws::kChunk) == 0 && kQRank % 32 == 0 && kQUp % 32 == 0, "tiles");
+constexpr int kQRow = kDNope + kDRope;   // 192 rows of W_UQ per head
+constexpr int kQUp = kHeads * kQRow;     // 24576
+using QDownPlan = ws::Plan<false, kQRank, kDHidden, 1, 7, 16, true>;
+using QUpPlan = ws::Plan<true, kQUp, kQRank, 3, 4, 1>;
+static_assert(kQRow % 4 == 0 && kDNope % 4 == 0, "4 columns never straddle a head or the nope/rope boundary");
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 __device__ __forceinline__ unsigned int bf16_rne(float x) {
   unsigned int u = __builtin_bit_cast(unsigned int, x);
@@ -39,75 +42,56 @@ __device__ __forceinline__ unsigned int bf16_rne(float x) {
   return u >> 16;
 }
 
-__global__ __launch_bounds__(256) void qdown_sum_kernel(const float* __restrict__ part, float* __restrict__ c_q,
-                                                        int rows) {
-  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;   // 4 values each
-  if (g * 4 >= (long long)rows * kQRank) return;
-  f32x4 s = *(const f32x4*)(part + g * 4);
+// q[r][c .. c + 3] (c % 4 == 0) -> q_nope / q_pe of token r, head c / 192
+struct HeadsEpi {
+  const int32_t* seq_lens;
+  uint16_t* q_nope;
+  uint16_t* q_pe;
+  int q_tokens;
+  double rope_base;
+  __device__ void operator()(int r, int c, f32x4 v) const {
+    const int head = c / kQRow, j = c % kQRow;
+    const size_t rh = (size_t)r * kHeads + head;
+    if (j < kDNope) {
+      const u32x2 p = {bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
+      *(u32x2*)(q_nope + rh * kDNope + j) = p;
+      return;
+    }
+    const int b = r / q_tokens, i = r % q_tokens;
+    const double pos = (double)(seq_lens[b] - q_tokens + i);
+    const int jr = j - kDNope;   // first of two position pairs
+    unsigned int w[2];
 #pragma unroll
-  for (int k = 1; k < kQDownSplit; ++k) {
-    const f32x4 v = *(const f32x4*)(part + (size_t)k * rows * kQRank + g * 4);
-    s += v;
+    for (int k = 0; k < 2; ++k) {
+      const int pair = jr / 2 + k;
+      const double theta = pow(rope_base, -2.0 * pair / kDRope);
+      double s, co;
+      sincos(pos * theta, &s, &co);
+      const double x0 = v[2 * k], x1 = v[2 * k + 1];
+      w[k] = bf16_rne((float)(x0 * co - x1 * s)) | (bf16_rne((float)(x0 * s + x1 * co)) << 16);
+    }
+    *(u32x2*)(q_pe + rh * kDRope + jr) = u32x2{w[0], w[1]};
   }
-  *(f32x4*)(c_q + g * 4) = s;
-}
-
-__global__ __launch_bounds__(256) void qfinish_kernel(const float* __restrict__ q, const int32_t* __restrict__ seq_lens,
-                                                      uint16_t* __restrict__ q_nope, uint16_t* __restrict__ q_pe,
-                                                      int rows, int q_tokens, double rope_base) {
-  constexpr int kPairs = kQRow / 2;   // 96 per head: 64 non-positional, 32 position
-  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (g >= (long long)rows * kHeads * kPairs) return;
-  const int pr = (int)(g % kPairs);
-  const long long rh = g / kPairs;   // row * 128 + head
-  const int r = (int)(rh / kHeads);
-  const f32x2 v = *(const f32x2*)(q + rh * kQRow + 2 * pr);
-  float y0 = v[0], y1 = v[1];
-  if (pr < kDNope / 2) {
-    *(unsigned int*)(q_nope + rh * kDNope + 2 * pr) = bf16_rne(y0) | (bf16_rne(y1) << 16);
-    return;
-  }
-  const int qq = pr - kDNope / 2;   // position pair
-  const int b = r / q_tokens, i = r % q_tokens;
-  const int pos = seq_lens[b] - q_tokens + i;
-  const double theta = pow(rope_base, -2.0 * qq / kDRope);
-  double s, c;
-  sincos((double)pos * theta, &s, &c);
-  const float z0 = (float)((double)y0 * c - (double)y1 * s);
-  const float z1 = (float)((double)y0 * s + (double)y1 * c);
-  *(unsigned int*)(q_pe + rh * kDRope + 2 * qq) = bf16_rne(z0) | (bf16_rne(z1) << 16);
-}
+};
 
 }  // namespace
 
 size_t qproj_workspace_bytes(int rows) {
-  return ((size_t)kQDownSplit * rows * kQRank + (size_t)rows * kQRank + (size_t)rows * kQUp) * sizeof(float);
+  return round256(QDownPlan::part_bytes(rows)) + round256(QUpPlan::packed_x_bytes(rows));
 }
 
 hipError_t launch_qproj(const uint16_t* hidden, const uint16_t* w_dq, const uint16_t* w_uq,
                         const int32_t* seq_lens, uint16_t* q_nope, uint16_t* q_pe, int batch,
-                        int q_tokens, double rope_base, float* ws, hipStream_t stream) {
+                        int q_tokens, double rope_base, void* ws, hipStream_t stream) {
   const int rows = batch * q_tokens;
-  float* part = ws;
-  float* c_q = part + (size_t)kQDownSplit * rows * kQRank;
-  float* q = c_q + (size_t)rows * kQRank;
-  hipLaunchKernelGGL((ws::wstream_kernel<false, kQDownPerWave>), dim3(kQRank / 32, kQDownSplit),
-                     dim3(ws::kThreads), 0, stream, (const void*)hidden, (long long)kDHidden, w_dq,
-                     (long long)kDHidden, part, (long long)kQRank, (long long)rows * kQRank, rows);
-  hipError_t e = hipGetLastError();
+  float* part = (float*)ws;
+  char* cq = (char*)ws + round256(QDownPlan::part_bytes(rows));
+  // c_Q rows past the batch in its last row tile are not written: a matrix
+  // product keeps tokens apart, so they only reach output rows that the
+  // epilogue never stores
+  const hipError_t e = QDownPlan::run(hidden, w_dq, part, rows, ws::StorePackedF32{cq, kQRank / 16}, stream);
   if (e != hipSuccess) return e;
-  const long long n4 = (long long)rows * kQRank / 4;
-  hipLaunchKernelGGL(qdown_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, part, c_q,
-                     rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((ws::wstream_kernel<true, kQRank / 4>), dim3(kQUp / 32, 1), dim3(ws::kThreads), 0,
-                     stream, (const void*)c_q, (long long)kQRank, w_uq, (long long)kQRank, q,
-                     (long long)kQUp, 0LL, rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long nf = (long long)rows * kHeads * (kQRow / 2);
-  hipLaunchKernelGGL(qfinish_kernel, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, stream, q, seq_lens,
-                     q_nope, q_pe, rows, q_tokens, rope_base);
-  return hipGetLastError();
+  return QUpPlan::run(cq, w_uq, nullptr, rows, HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rope_base}, stream);
 }
 
 }  // namespace mla

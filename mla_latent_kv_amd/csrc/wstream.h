@@ -1,22 +1,40 @@
 // Weight-stream product for a few dozen tokens:
-//   D[split][t][n] = sum_{k in the split's K range} W[n][k] x[t][k]
-// W bf16 [N][ldw] row-major, x bf16 or fp32 [tokens][ldx] row-major, D fp32.
-// Every W byte is used by only the batch's tokens, so the bound is HBM on W.
+//   D[t][n] = sum_k W[n][k] x[t][k]
+// with W bf16 [N][K] and x bf16 or fp32 [tokens][K]. Every weight byte is used
+// by only the batch's tokens, so the bound is HBM on W.
 //
-// Workgroup = 32 columns (n) x one K range; its 4 wavefronts split the range
-// (kKPerWave each) and each streams its weight and input tiles (chunks of 64
-// k) through its own 3-stage LDS ring with direct-to-LDS fetches laid out so
-// that every 1 KB fetch covers 8 whole cache lines (fragments loaded straight
-// from global memory touch 32 rows per instruction and starve the load path).
-// Two chunks stay in flight per wavefront; the waits are explicit and the
-// loop has no barrier. 32x32x16 bf16 MFMA, fp32 accumulation; an fp32 input
-// enters as x = hi + lo (hi = bf16(x), lo = bf16(x - hi): within 2^-17 of x),
-// two MFMAs per k-step. The 4 wavefront tiles are summed in LDS in a fixed
-// order (deterministic) and stored as fp32 at
-//   out + blockIdx.y * out_split + t * ldo + n.
-// Grid: (N / 32, number of K splits); split s covers k in
-// [s * 4 * kKPerWave, (s + 1) * 4 * kKPerWave). More than 32 tokens loop over
-// row tiles (each re-streams the slice).
+// Layouts. The matrix cores take 32x32x16 bf16 steps: operand A (the weight)
+// is one 16-byte fragment per lane, lane l holding row n = l % 32 and the 8
+// consecutive k at 8 (l / 32) of a 16-wide k-step. Both operands are stored
+// in that fragment order, so that every wavefront load is one contiguous
+// 1 KB (8 whole cache lines) and goes straight into registers:
+//  * packed weight (made once, at load time, by pack_w_kernel): the 1 KB block
+//    of column tile ct (32 rows of W) and k-step ks sits at byte
+//    (ks * N/32 + ct) * 1024; lane l's 16 bytes are W[32 ct + l % 32][16 ks +
+//    8 (l / 32) .. + 7]. The k-step is the outer index: the wavefronts that
+//    stream one K range at the same time read one compact address window.
+//  * packed input (per call, pack_x_kernel, or written in this order by the
+//    producing epilogue): row tile rt (32 tokens), k-step ks; bf16: 1 KB at
+//    (rt * K/16 + ks) * 1024, lane l: x[32 rt + l % 32][16 ks + 8 (l / 32) ..
+//    + 7]; fp32: 2 KB at (rt * K/16 + ks) * 2048, half q at + 1024 q, lane l:
+//    x[32 rt + l % 32][16 ks + 8 (l / 32) + 4 q .. + 3]. Tokens past the batch
+//    are zero.
+//
+// stream_kernel: workgroup = kCT column tiles (32 kCT columns) x one K range
+// of one row tile; its 4 wavefronts split the range (ks_per_wave k-steps
+// each). Each wavefront keeps kDepth k-steps of fragments in flight in a
+// register ring (weights with non-temporal loads, so that they do not evict
+// the inputs that every column block re-reads), no LDS and no barrier in the
+// loop. fp32 inputs enter as x = hi + lo (hi = bf16(x), lo = bf16(x - hi),
+// together within 2^-17 of x), two MFMAs per k-step; accumulation in fp32.
+// The 4 wavefront tiles are summed in LDS in a fixed order. With one K split
+// the epilogue receives the finished values; with several each split stores
+// its partial tile and sum_kernel adds the splits in split order and calls the
+// epilogue. No atomics: results are deterministic. (A split-K finish inside
+// the stream, the last workgroup of a column block adding the others' tiles,
+// needs device-scope release/acquire fences between workgroups on different
+// XCDs; they write back and invalidate the whole L2 and measured slower than
+// the separate sum.)
 #pragma once
 
 #include "common.h"
@@ -25,33 +43,6 @@ namespace mla {
 namespace ws {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;                     // k per staged chunk (4 k-steps)
-constexpr int kRing = 3;                       // chunks resident per wavefront
-constexpr int kWTile = 32 * kChunk * 2;        // 4 KB: 32 weight rows x 64 bf16
-
-template <bool kXF32>
-struct Tiles {
-  static constexpr int kXTile = 32 * kChunk * (kXF32 ? 4 : 2);   // inputs of 32 tokens
-  static constexpr int kStage = kWTile + kXTile;
-  static constexpr int kWaveLds = kRing * kStage;
-  static constexpr int kLds = 4 * kWaveLds;
-  static constexpr int kDmaPerChunk = (kWTile + kXTile) / 1024;
-};
-
-#define WS_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
-#define WS_WAIT_LGKM0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
-
-// One direct-to-LDS fetch: 64 lanes x 16 bytes from base + voff (per lane) to
-// LDS bytes [lds, lds + 1024), lane l at lds + 16 l. Inline asm so that the
-// compiler does not drain it before every LDS read; the kernel orders it with
-// its own waits. No VGPR result.
-__device__ __forceinline__ void dma16(const char* lds, const char* base, unsigned voff) {
-  const unsigned m0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(base)
-               : "m0");
-}
 
 __device__ __forceinline__ void split_bf16(const f32x4 a, const f32x4 b, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -66,113 +57,243 @@ __device__ __forceinline__ void split_bf16(const f32x4 a, const f32x4 b, bf16x8&
   }
 }
 
-template <bool kXF32, int kKPerWave>
-__global__ __launch_bounds__(kThreads, 1) void wstream_kernel(const void* __restrict__ x, long long ldx,
-                                                              const uint16_t* __restrict__ w,
-                                                              long long ldw, float* __restrict__ out,
-                                                              long long ldo, long long out_split,
-                                                              int rows) {
-  using T = Tiles<kXF32>;
-  constexpr int kChunks = kKPerWave / kChunk;
-  constexpr int kXBytes = kXF32 ? 4 : 2;
-  static_assert(kKPerWave % kChunk == 0, "whole chunks");
-  static_assert(T::kLds <= 160 * 1024, "LDS of one gfx950 workgroup");
-  __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
-  const int t = threadIdx.x, lane = t & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int n0 = blockIdx.x * 32;
-  const long long kw = (long long)blockIdx.y * 4 * kKPerWave + (long long)wv * kKPerWave;
-  char* ring = smem + wv * T::kWaveLds;
+// Byte offset of the 16-byte piece holding x[r][c .. c + 3] (c % 4 == 0) in
+// the packed fp32 input layout of a K-wide input (k_steps = K / 16).
+__device__ __forceinline__ size_t packed_f32_piece(int r, int c, int k_steps) {
+  const int rt = r >> 5, n = r & 31, ks = c >> 4, h = (c >> 3) & 1, q = (c >> 2) & 1;
+  return (((size_t)rt * k_steps + ks) * 2 + q) * 1024 + 16 * (n + 32 * h);
+}
 
-  // Weight tile, fetch i (0..3): lane = (row 8 i + lane / 8, 16-byte piece
-  // lane % 8 of the row's 128 bytes): 8 whole cache lines per fetch. Offsets
-  // are relative to the tile's first row and the wavefront's first k, which
-  // go into the scalar base with the chunk advance.
-  unsigned voff_w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voff_w[i] = (unsigned)(((8 * i + (lane >> 3)) * ldw + 8 * (lane & 7)) * 2);
-  const char* w_tile = (const char*)(w + (size_t)n0 * ldw + kw);
-
-  for (int r0 = 0; r0 < rows; r0 += 32) {
-    // Input tile: fp32 rows are 256 bytes per chunk (fetch i: token
-    // 4 i + lane / 16, piece lane % 16), bf16 rows 128 bytes (fetch i: token
-    // 8 i + lane / 8, piece lane % 8). Tokens past the batch read the tile's
-    // first token: their columns of D are never stored.
-    constexpr int kXFetch = T::kXTile / 1024;
-    unsigned voff_x[kXFetch];
-#pragma unroll
-    for (int i = 0; i < kXFetch; ++i) {
-      const int tt = kXF32 ? 4 * i + (lane >> 4) : 8 * i + (lane >> 3);
-      const int piece = kXF32 ? (lane & 15) : (lane & 7);
-      voff_x[i] = (unsigned)(((r0 + tt < rows ? tt : 0) * ldx) * kXBytes + 16 * piece);
-    }
-    const char* x_tile = (const char*)x + ((size_t)r0 * ldx + kw) * kXBytes;
-    auto fetch = [&](int c) {   // chunk c (clamped to the last) into its ring stage
-      const int cc = c < kChunks ? c : kChunks - 1;
-      char* st = ring + (c % kRing) * T::kStage;
-      const char* wb = w_tile + (size_t)cc * kChunk * 2;
-      const char* xb = x_tile + (size_t)cc * kChunk * kXBytes;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(st + 1024 * i, wb, voff_w[i]);
-#pragma unroll
-      for (int i = 0; i < kXFetch; ++i) dma16(st + kWTile + 1024 * i, xb, voff_x[i]);
-    };
-#pragma unroll
-    for (int c = 0; c < kRing; ++c) fetch(c);
-
-    // fragments: A (lane = column n, half h): row n, k 16 j + 8 h; B (lane =
-    // token, half h): token, k 16 j + 8 h
+// Packs the input: workgroup = one row tile x kPackSteps k-steps. The 32
+// rows' slices are read with whole-row-segment loads into LDS, then written
+// out in the packed order (one contiguous block of kPackSteps pieces of 1 or
+// 2 KB). Tokens past `rows` are written as zeros.
+constexpr int kPackSteps = 8;
+template <bool kXF32>
+__global__ __launch_bounds__(256) void pack_x_kernel(const void* __restrict__ x, u32x4* __restrict__ p, int rows,
+                                                     int k_steps) {
+  constexpr int kEl = kXF32 ? 4 : 2;                       // bytes per element
+  constexpr int kRowBytes = kPackSteps * 16 * kEl;         // a row's slice: 512 or 256 bytes
+  constexpr int kPieces = 32 * kRowBytes / 16;             // 16-byte pieces in the tile
+  __shared__ u32x4 tile[32][kRowBytes / 16 + 1];           // padded rows
+  const int rt = blockIdx.y, ks0 = blockIdx.x * kPackSteps, t = threadIdx.x;
+  const size_t ld = (size_t)16 * k_steps * kEl;            // bytes per input row
+  for (int i = t; i < kPieces; i += 256) {
+    const int row = i / (kRowBytes / 16), pc = i % (kRowBytes / 16);
+    const int r = 32 * rt + row;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows) v = *(const u32x4*)((const char*)x + (size_t)r * ld + (size_t)ks0 * 16 * kEl + 16 * pc);
+    tile[row][pc] = v;
+  }
+  __syncthreads();
+  // piece i of the output block: k-step j, (half q), lane l = n + 32 h
+  for (int i = t; i < kPieces; i += 256) {
+    const int per = kXF32 ? 128 : 64;
+    const int j = i / per, rem = i % per, q = kXF32 ? rem / 64 : 0, lane = rem % 64;
     const int n = lane & 31, h = lane >> 5;
-    const int a_off = (n >> 3) * 1024 + (n & 7) * 128 + 16 * h;
-    const int b_off = kXF32 ? kWTile + (n >> 2) * 1024 + (n & 3) * 256 + 32 * h
-                            : kWTile + (n >> 3) * 1024 + (n & 7) * 128 + 16 * h;
-    f32x16 acc = {};
-    for (int c = 0; c < kChunks; ++c) {
-      // chunk c is in: at most the two younger chunks' fetches remain
-      if constexpr (kXF32) {
-        WS_WAIT_VM(24);
-      } else {
-        WS_WAIT_VM(16);
-      }
-      const char* st = ring + (c % kRing) * T::kStage;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + a_off + 32 * j));
-        if constexpr (kXF32) {
-          const f32x4 xa = *(const f32x4*)(st + b_off + 64 * j);
-          const f32x4 xb = *(const f32x4*)(st + b_off + 64 * j + 16);
-          bf16x8 hi, lo;
-          split_bf16(xa, xb, hi, lo);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo, acc, 0, 0, 0);
-        } else {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + b_off + 32 * j));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-        }
-      }
-      WS_WAIT_LGKM0();        // this stage's reads are done before its refill lands
-      fetch(c + kRing);       // past the end: the last chunk again, into a spent stage
-    }
-    WS_WAIT_VM(0);
-    __syncthreads();   // every wavefront is done with its ring: reuse it for the sum
-    float(*red)[32][33] = (float(*)[32][33])smem;   // [wave][column][token]
-    // acc[i] is column 8 (i / 4) + 4 (lane / 32) + i % 4 of token lane % 32
-#pragma unroll
-    for (int i = 0; i < 16; ++i) red[wv][8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][lane & 31] = acc[i];
-    __syncthreads();
-    {
-      const int rr = t >> 3, nq = (t & 7) * 4;   // token, first of 4 columns
-      if (r0 + rr < rows) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = ((red[0][nq + e][rr] + red[1][nq + e][rr]) + red[2][nq + e][rr]) + red[3][nq + e][rr];
-        *(f32x4*)(out + (size_t)blockIdx.y * out_split + (size_t)(r0 + rr) * ldo + n0 + nq) = v;
-      }
-    }
-    __syncthreads();
+    const int pc = (j * 16 + 8 * h + 4 * q) * kEl / 16;   // 16-byte piece within the row slice
+    p[((size_t)rt * k_steps + ks0) * per + i] = tile[n][pc];
   }
 }
+
+struct StreamArgs {
+  const u32x4* xp;    // packed input
+  const u32x4* wp;    // packed weight
+  int n_tiles;        // N / 32
+  int k_steps;        // K / 16
+  int rows;           // tokens
+  int ks_per_wave;    // k-steps per wavefront (a multiple of kDepth, >= kDepth)
+};
+
+template <bool kXF32, int kCT>
+struct Step {
+  u32x4 w[kCT];
+  u32x4 x[kXF32 ? 2 : 1];
+};
+
+// Grid (n_tiles / kCT, splits, row tiles). Wavefront w of workgroup (cb, s)
+// covers k-steps [(4 s + w) * ks_per_wave, + ks_per_wave). Epi is called as
+// epi(r, c, v) with v = D[r][c .. c + 3], c % 4 == 0, only for r < rows.
+// kXRows: a bf16 input read straight from its row-major rows (lane (n, h)
+// loads its 16 bytes from row n: 32 rows per load instead of 8 cache lines,
+// which costs little where the input is small and L2-resident and the stream
+// is short, and saves the packing launch); rows past the batch read row 0.
+template <bool kXF32, int kCT, int kDepth, bool kXRows, class Epi>
+__global__ __launch_bounds__(kThreads, 1) void stream_kernel(StreamArgs a, Epi epi) {
+  static_assert(!(kXF32 && kXRows), "row-major input only for bf16");
+  __shared__ float red[4][kCT * 32][33];   // [wave][column][token], padded
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int cb = blockIdx.x, rt = blockIdx.z;
+  const int ks0 = (blockIdx.y * 4 + wv) * a.ks_per_wave;
+  const int n = lane & 31, h = lane >> 5;
+  constexpr int kXPer = kXF32 ? 128 : 64;   // 16-byte pieces per input k-step
+  const u32x4* wbase = a.wp + (size_t)cb * kCT * 64 + lane;
+  const size_t wstep = (size_t)a.n_tiles * 64;
+  const u32x4* xbase =
+      kXRows ? (const u32x4*)((const uint16_t*)a.xp +
+                              (size_t)(32 * rt + n < a.rows ? 32 * rt + n : 0) * (16 * (size_t)a.k_steps) +
+                              16 * (size_t)ks0 + 8 * h)
+             : a.xp + ((size_t)rt * a.k_steps + ks0) * kXPer + lane;
+  constexpr int kXStep = kXRows ? 2 : kXPer;   // 16-byte units from one k-step to the next
+
+  Step<kXF32, kCT> ring[kDepth];
+  auto load = [&](Step<kXF32, kCT>& st, int s) {
+    const u32x4* wb = wbase + (size_t)(ks0 + s) * wstep;
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) st.w[j] = __builtin_nontemporal_load(wb + 64 * j);
+    const u32x4* xb = xbase + (size_t)s * kXStep;
+    st.x[0] = xb[0];
+    if constexpr (kXF32) st.x[1] = xb[64];
+  };
+  f32x16 acc[kCT];
+#pragma unroll
+  for (int j = 0; j < kCT; ++j) acc[j] = f32x16{};
+  auto compute = [&](const Step<kXF32, kCT>& st) {
+    if constexpr (kXF32) {
+      bf16x8 hi, lo;
+      split_bf16(__builtin_bit_cast(f32x4, st.x[0]), __builtin_bit_cast(f32x4, st.x[1]), hi, lo);
+#pragma unroll
+      for (int j = 0; j < kCT; ++j) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, st.w[j]);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, hi, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, lo, acc[j], 0, 0, 0);
+      }
+    } else {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, st.x[0]);
+#pragma unroll
+      for (int j = 0; j < kCT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.w[j]), b, acc[j], 0, 0,
+                                                         0);
+    }
+  };
+  // The scheduling barriers keep every step's loads in issue order (the
+  // compiler otherwise sinks the refills to the end of the unrolled round and
+  // drains the ring): each step's wait leaves the kDepth - 1 younger steps in
+  // flight.
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    load(ring[d], d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int s = 0; s < a.ks_per_wave - kDepth; s += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      compute(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ring[d], s + d + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) compute(ring[d]);
+
+  // acc[j][i] is column 32 j + 8 (i / 4) + 4 h + i % 4 of token n
+#pragma unroll
+  for (int j = 0; j < kCT; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wv][32 * j + 8 * (i >> 2) + 4 * h + (i & 3)][n] = acc[j][i];
+  __syncthreads();
+  const int c0 = cb * kCT * 32;
+  for (int e = t; e < 32 * kCT * 8; e += kThreads) {   // (token, 4 columns)
+    const int rr = e / (kCT * 8), c4 = (e % (kCT * 8)) * 4;
+    const int r = 32 * rt + rr;
+    if (r >= a.rows) continue;
+    f32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = ((red[0][c4 + q][rr] + red[1][c4 + q][rr]) + red[2][c4 + q][rr]) + red[3][c4 + q][rr];
+    epi(r, c0 + c4, v);
+  }
+}
+
+// A K split's partial sums: [split][rows][n] fp32, split = blockIdx.y.
+struct StorePartial {
+  float* part;
+  int rows, n;
+  __device__ void operator()(int r, int c, f32x4 v) const {
+    *(f32x4*)(part + ((size_t)blockIdx.y * rows + r) * n + c) = v;
+  }
+};
+
+// Sums the K splits in split order: one thread per (token, 4 columns); all
+// of a thread's loads are issued before the first add.
+template <int kSplits, class Epi>
+__global__ __launch_bounds__(256) void sum_kernel(const float* __restrict__ part, int rows, int n, Epi epi) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (long long)rows * (n / 4)) return;
+  const int r = (int)(g / (n / 4)), c = (int)(g % (n / 4)) * 4;
+  const size_t split = (size_t)rows * n;
+  f32x4 u[kSplits];
+#pragma unroll
+  for (int s = 0; s < kSplits; ++s) u[s] = *(const f32x4*)(part + s * split + (size_t)r * n + c);
+  f32x4 v = u[0];
+#pragma unroll
+  for (int s = 1; s < kSplits; ++s) v += u[s];
+  epi(r, c, v);
+}
+
+// Host side: a product's shape and tiling, fixed at compile time. kXRows:
+// the (bf16) input is passed row-major, without the packing launch.
+template <bool kXF32, int kN, int kK, int kCT, int kDepth, int kSplits, bool kXRows = false>
+struct Plan {
+  static constexpr int kNTiles = kN / 32, kKSteps = kK / 16;
+  static constexpr int kKsPerWave = kKSteps / (4 * kSplits);
+  static_assert(kN % (32 * kCT) == 0, "whole column blocks");
+  static_assert(kKSteps % (4 * kSplits) == 0, "whole k-steps per wavefront");
+  static_assert(kKsPerWave % kDepth == 0 && kKsPerWave >= kDepth, "whole ring rounds");
+  static_assert(4 * kCT * 32 * 33 * 4 <= 160 * 1024, "LDS of one gfx950 workgroup");
+
+  static size_t packed_x_bytes(int rows) {
+    return kXRows ? 0 : (size_t)((rows + 31) / 32) * 32 * kK * (kXF32 ? 4 : 2);
+  }
+  static size_t part_bytes(int rows) { return kSplits > 1 ? (size_t)kSplits * rows * kN * sizeof(float) : 0; }
+
+  static hipError_t pack_x(const void* x, void* xp, int rows, hipStream_t stream) {
+    static_assert(!kXRows, "a row-major input is not packed");
+    static_assert(kKSteps % kPackSteps == 0, "whole packing tiles");
+    hipLaunchKernelGGL(pack_x_kernel<kXF32>, dim3(kKSteps / kPackSteps, (rows + 31) / 32), dim3(256), 0, stream, x,
+                       (u32x4*)xp, rows, kKSteps);
+    return hipGetLastError();
+  }
+  // The product of the input xp (packed, or row-major with kXRows) and the
+  // packed weight wp, finished by
+  // epi: one launch with one split, else the stream into `part`
+  // (part_bytes(rows)) and the split-order sum.
+  template <class Epi>
+  static hipError_t run(const void* xp, const void* wp, float* part, int rows, Epi epi, hipStream_t stream) {
+    const StreamArgs a{(const u32x4*)xp, (const u32x4*)wp, kNTiles, kKSteps, rows, kKsPerWave};
+    const dim3 grid(kNTiles / kCT, kSplits, (rows + 31) / 32);
+    if constexpr (kSplits == 1) {
+      hipLaunchKernelGGL((stream_kernel<kXF32, kCT, kDepth, kXRows, Epi>), grid, dim3(kThreads), 0, stream, a,
+                         epi);
+      return hipGetLastError();
+    } else {
+      hipLaunchKernelGGL((stream_kernel<kXF32, kCT, kDepth, kXRows, StorePartial>), grid, dim3(kThreads), 0,
+                         stream, a, StorePartial{part, rows, kN});
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long items = (long long)rows * (kN / 4);
+      hipLaunchKernelGGL((sum_kernel<kSplits, Epi>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
+                         part, rows, kN, epi);
+      return hipGetLastError();
+    }
+  }
+};
+
+// fp32 rows of `ld` floats.
+struct StoreF32 {
+  float* out;
+  long long ld;
+  __device__ void operator()(int r, int c, f32x4 v) const { *(f32x4*)(out + (size_t)r * ld + c) = v; }
+};
+
+// The packed fp32 input layout of a following product with k_steps = N / 16.
+struct StorePackedF32 {
+  char* out;
+  int k_steps;
+  __device__ void operator()(int r, int c, f32x4 v) const { *(f32x4*)(out + packed_f32_piece(r, c, k_steps)) = v; }
+};
 
 }  // namespace ws
 }  // namespace mla

@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported():
                         "mla_decode_run_profiled", "mla_decode_destroy",
                         "mla_decode_status_string", "mla_cache_append",
                         "mla_cache_append_workspace_size", "mla_output_project",
-                        "mla_query_project", "mla_query_project_workspace_size"}
+                        "mla_output_project_workspace_size", "mla_query_project",
+                        "mla_query_project_workspace_size", "mla_pack_weight"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -96,9 +97,16 @@ def test_output_project_rejects_nulls_before_any_device_call():
     import ctypes
     from mla_latent_kv_amd import binding
     lib = _lib()
+    n = ctypes.c_size_t()
+    assert lib.mla_output_project_workspace_size(None, 4, ctypes.byref(n)) == -1
     args = binding.MlaOprojArgs()
-    assert lib.mla_output_project(None, ctypes.byref(args), None) == -1
-    assert lib.mla_output_project(None, None, None) == -1
+    assert lib.mla_output_project(None, ctypes.byref(args), None, 0, None) == -1
+    assert lib.mla_output_project(None, None, None, 0, None) == -1
+
+
+def test_pack_weight_rejects_nulls_before_any_device_call():
+    lib = _lib()
+    assert lib.mla_pack_weight(None, None, None, 32, 16, None) == -1
 
 
 def test_query_project_rejects_nulls_before_any_device_call():

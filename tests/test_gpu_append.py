@@ -46,8 +46,9 @@ def _run_append(batch, inp, rope_base=0.0):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
     dec = binding.MLADecoder(0, max_q_tokens=2)
-    dec.append(bf16(inp["hidden"]), bf16(inp["w_dkv"]), bf16(inp["w_kr"]), d["kv_cache"],
-               d["block_table"], d["seq_lens"], rope_base=rope_base)
+    w_kv = dec.pack(bf16(np.concatenate([inp["w_dkv"], inp["w_kr"]])))   # stacked [W_DKV; W_KR]
+    dec.append(bf16(inp["hidden"]), w_kv, d["kv_cache"], d["block_table"], d["seq_lens"],
+               rope_base=rope_base)
     torch.cuda.synchronize()
     cache = d["kv_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
     dec.close()

@@ -27,7 +27,7 @@ def _run(x, w_bits):
     import torch
     from mla_latent_kv_amd import binding
     dec = binding.MLADecoder(0, max_q_tokens=2)
-    y = dec.output_project(torch.from_numpy(np.ascontiguousarray(x)).cuda(), _w_o_tensor(w_bits))
+    y = dec.output_project(torch.from_numpy(np.ascontiguousarray(x)).cuda(), dec.pack(_w_o_tensor(w_bits)))
     torch.cuda.synchronize()
     dec.close()
     return y.cpu().numpy().astype(np.float64)

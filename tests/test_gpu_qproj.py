@@ -36,7 +36,7 @@ def _run_q(inp, seq_lens):
     import torch
     from mla_latent_kv_amd import binding
     dec = binding.MLADecoder(0, max_q_tokens=2)
-    qn, qp = dec.query_project(_t(inp["hidden"]), _t(inp["w_dq"]), _t(inp["w_uq"]),
+    qn, qp = dec.query_project(_t(inp["hidden"]), dec.pack(_t(inp["w_dq"])), dec.pack(_t(inp["w_uq"])),
                                torch.from_numpy(np.ascontiguousarray(seq_lens)).cuda())
     torch.cuda.synchronize()
     dec.close()
@@ -102,12 +102,13 @@ def test_attention_block_end_to_end():
     say("case attention block B=3 Sq=2")
     d = device.upload(batch)
     dec = binding.MLADecoder(0, max_q_tokens=2)
-    dec.append(_t(app["hidden"]), _t(app["w_dkv"]), _t(app["w_kr"]), d["kv_cache"],
-               d["block_table"], d["seq_lens"])
-    qn, qp = dec.query_project(_t(hid["hidden"]), _t(hid["w_dq"]), _t(hid["w_uq"]), d["seq_lens"])
+    w_kv = dec.pack(_t(np.concatenate([app["w_dkv"], app["w_kr"]])))
+    w_dq, w_uq, w_o_p = dec.pack(_t(hid["w_dq"])), dec.pack(_t(hid["w_uq"])), dec.pack(_t(w_o))
+    dec.append(_t(app["hidden"]), w_kv, d["kv_cache"], d["block_table"], d["seq_lens"])
+    qn, qp = dec.query_project(_t(hid["hidden"]), w_dq, w_uq, d["seq_lens"])
     out = dec(qn, qp, d["w_uk"], d["w_uv"], d["kv_cache"], d["block_table"], d["seq_lens"],
               d["max_seq_len"])
-    y = dec.output_project(out, _t(w_o))
+    y = dec.output_project(out, w_o_p)
     torch.cuda.synchronize()
     got = y.cpu().numpy().astype(np.float64)
     dec.close()
