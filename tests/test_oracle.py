@@ -277,3 +277,45 @@ def test_bf16_decode_is_exact():
     back = orc.bf16_bits_to_f64(bits)
     assert back[1] == 1.0 and back[2] == -2.5 and back[3] == 3.140625
     assert abs(back[4] - 1e-3) <= 2 ** -9 * 1e-3
+
+
+# --------------------------------------------------------------------------
+# Prefill: every prompt token is a query (Sq = L), attention is causal.
+
+def test_prefill_reduces_to_library_causal_attention():
+    """Sq = L with selection weights is plain causal attention: torch's
+    scaled_dot_product_attention with its own is_causal rule (query i sees
+    keys 0..i when the query and key counts agree), fp64 on the CPU."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(61)
+    H, L = 3, 150
+    qn, qp, _, _, c, kr = _full_dims_case(rng, n_heads=H, length=L, sq=L)
+    a, b = [64, 0, 300], [0, 384, 200]
+    wk = np.zeros((H, 128, 512))
+    wv = np.zeros((H, 128, 512))
+    for h in range(H):
+        wk[h, np.arange(128), a[h] + np.arange(128)] = 1.0
+        wv[h, np.arange(128), b[h] + np.arange(128)] = 1.0
+    scale = orc.default_scale()
+    got = orc.naive_decode(qn, qp, wk, wv, c, kr, scale)
+    for h in range(H):
+        q = torch.tensor(np.concatenate([qn[:, h], qp[:, h]], axis=1))[None]
+        k = torch.tensor(np.concatenate([c[:, a[h]:a[h] + 128], kr], axis=1))[None]
+        v = torch.tensor(c[:, b[h]:b[h] + 128])[None]
+        want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)[0]
+        assert np.max(np.abs(got[:, h] - want.numpy())) <= 1e-12 * float(want.abs().max())
+
+
+def test_prefill_row_equals_decode_of_its_prefix():
+    """Prompt token i of a prefill sees exactly positions 0..i: the same
+    result as a one-token decode of the first i + 1 cached tokens."""
+    rng = np.random.default_rng(62)
+    L = 70
+    qn, qp, wk, wv, c, kr = _full_dims_case(rng, n_heads=2, length=L, sq=L)
+    scale = orc.default_scale()
+    full = orc.naive_decode(qn, qp, wk, wv, c, kr, scale)
+    for i in (0, 1, 31, 63, 64, 69):
+        one = orc.naive_decode(qn[i:i + 1], qp[i:i + 1], wk, wv, c[:i + 1], kr[:i + 1], scale)
+        assert np.max(np.abs(full[i] - one[0])) <= 1e-12 * np.max(np.abs(one))
+    # the first prompt token attends only to itself: its output is its own value
+    np.testing.assert_allclose(full[0], np.einsum("hvc,c->hv", wv, c[0]), rtol=1e-12, atol=1e-13)
