@@ -49,7 +49,8 @@ Readings where the pages are silent or garbled (each is repeated in the design doc):
   q_pe = RoPE(q[128:], L - Sq + i). No normalisation of c_Q (the pages give
   none).
 * with Sq new tokens per sequence (all already in the cache, counted in L),
-  query i sees cached positions j <= L - Sq + i.
+  query i sees cached positions j <= L - Sq + i; a row that sees no position
+  (L < Sq, i < Sq - L) yields zeros (no page covers it).
 * k_R is one 64-d key per token shared by every head ([P5] section 2.3).
 * W_UK[h], W_UV[h] are [128, 512]: k = W_UK[h] c, v = W_UV[h] c.
 
@@ -160,7 +161,8 @@ def naive_decode(q_nope, q_pe, w_uk, w_uv, c_kv, k_r, scale, heads=None,
         p = np.zeros_like(s)
         for i in range(sq):
             n = visible_len(length, sq, i)
-            p[i, :n] = softmax(s[i, :n])
+            if n > 0:               # a row that sees no position keeps p = 0: output 0
+                p[i, :n] = softmax(s[i, :n])
         acc = np.zeros((sq, w_uv.shape[1]))
         for t0 in range(0, length, chunk):
             t1 = min(length, t0 + chunk)

@@ -319,3 +319,19 @@ def test_prefill_row_equals_decode_of_its_prefix():
         assert np.max(np.abs(full[i] - one[0])) <= 1e-12 * np.max(np.abs(one))
     # the first prompt token attends only to itself: its output is its own value
     np.testing.assert_allclose(full[0], np.einsum("hvc,c->hv", wv, c[0]), rtol=1e-12, atol=1e-13)
+
+
+def test_rows_that_see_nothing_are_zero_and_the_rest_unchanged():
+    """L < Sq: rows i < Sq - L see no position and yield zeros (the reading
+    the C ABI states); row i >= Sq - L sees positions 0..L-Sq+i, exactly a
+    one-token decode of that prefix."""
+    rng = np.random.default_rng(63)
+    L, sq = 5, 9
+    qn, qp, wk, wv, c, kr = _full_dims_case(rng, n_heads=2, length=L, sq=sq)
+    scale = orc.default_scale()
+    got = orc.naive_decode(qn, qp, wk, wv, c, kr, scale)
+    assert np.all(got[:sq - L] == 0.0)
+    for i in range(sq - L, sq):
+        n = L - sq + i + 1
+        one = orc.naive_decode(qn[i:i + 1], qp[i:i + 1], wk, wv, c[:n], kr[:n], scale)
+        assert np.max(np.abs(got[i] - one[0])) <= 1e-12 * np.max(np.abs(one))
