@@ -120,15 +120,16 @@ def visible_len(length: int, sq: int, i: int) -> int:
 # Naive path: materialise per-head K and V ([P3] naive branch; [P5] 2.1, 2.3).
 
 def naive_scores(q_nope_h, q_pe_h, w_uk_h, c_kv, k_r, scale):
-    """Scores of one query (one head) against every given cached token.
+    """Scores of query rows (one head) against every given cached token.
 
     K_h[j] = [W_UK[h] c_j ; k_R,j] (192 wide), q_h = [q_nope ; q_pe];
-    s_j = scale * q_h . K_h[j].
+    s_j = scale * q_h . K_h[j]. q_nope_h [..., 128], q_pe_h [..., 64] (one
+    query or a block of them); returns [..., L].
     """
-    k_nope = c_kv @ w_uk_h.T                       # [L, 128]: W_UK[h] c_j per row
-    k_full = np.concatenate([k_nope, k_r], axis=1)  # [L, 192]
-    q_full = np.concatenate([q_nope_h, q_pe_h])     # [192]
-    return scale * (k_full @ q_full)
+    k_nope = c_kv @ w_uk_h.T                                    # [L, 128]: W_UK[h] c_j per row
+    k_full = np.concatenate([k_nope, k_r], axis=1)               # [L, 192]
+    q_full = np.concatenate([q_nope_h, q_pe_h], axis=-1)         # [..., 192]
+    return scale * (q_full @ k_full.T)
 
 
 def softmax(s: np.ndarray) -> np.ndarray:
@@ -151,13 +152,12 @@ def naive_decode(q_nope, q_pe, w_uk, w_uv, c_kv, k_r, scale, heads=None,
     heads = range(n_heads) if heads is None else heads
     out = np.full((sq, n_heads, w_uv.shape[1]), np.nan)
     for h in heads:
-        # scores for all queries of this head; K_h chunk by chunk
+        # scores for all queries of this head; K_h chunk by chunk, each chunk
+        # materialised once for every query row
         s = np.empty((sq, length))
         for t0 in range(0, length, chunk):
             t1 = min(length, t0 + chunk)
-            for i in range(sq):
-                s[i, t0:t1] = naive_scores(q_nope[i, h], q_pe[i, h], w_uk[h],
-                                           c_kv[t0:t1], k_r[t0:t1], scale)
+            s[:, t0:t1] = naive_scores(q_nope[:, h], q_pe[:, h], w_uk[h], c_kv[t0:t1], k_r[t0:t1], scale)
         p = np.zeros_like(s)
         for i in range(sq):
             n = visible_len(length, sq, i)

@@ -38,14 +38,14 @@ def _brute_tiny_mismatch(monkeypatch, patch):
 def test_dropped_rope_term_is_caught(monkeypatch):
     def patch(m):
         m.setattr(orc, "naive_scores",
-                  lambda qn, qp, wk, c, kr, s: s * ((c @ wk.T) @ qn))
+                  lambda qn, qp, wk, c, kr, s: s * (qn @ (c @ wk.T).T))
     assert _brute_tiny_mismatch(monkeypatch, patch) > 1e-3
 
 
 def test_wrong_rope_sign_is_caught(monkeypatch):
     def patch(m):
         m.setattr(orc, "naive_scores",
-                  lambda qn, qp, wk, c, kr, s: s * ((c @ wk.T) @ qn - kr @ qp))
+                  lambda qn, qp, wk, c, kr, s: s * (qn @ (c @ wk.T).T - qp @ kr.T))
     assert _brute_tiny_mismatch(monkeypatch, patch) > 1e-3
 
 
