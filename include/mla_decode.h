@@ -281,6 +281,55 @@ int mla_output_project_workspace_size(const mla_decode_ctx* ctx, int32_t rows, s
 int mla_output_project(const mla_decode_ctx* ctx, const mla_oproj_args* args, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---- Naive path (materialised keys and values; prefill) -------------------
+ *
+ * The same attention as mla_decode_run, computed the other way round: per
+ * head the keys K_h[j] = [W_UK[h] c_j ; k_R,j] (192 wide) and values
+ * V_h[j] = W_UV[h] c_j (128) are materialised from the latent cache, then a
+ * standard softmax attention runs over them ("DeepSeek-V3" page at
+ * ailearn.mscapital.top, MLA paragraphs: the naive branch, which expands the
+ * per-token cache to 128 x (192 + 128) = 40,960 elements; "DeepSeek-V3"
+ * article at m.lsln.cn, section 2.1). Any number of query tokens: with
+ * q_tokens = L every prompt token is a query (prefill, causal, quadratic in
+ * L). Visibility, scale and the zero rule are those of mla_decode_run (row i
+ * of sequence b sees positions j <= L_b - q_tokens + i; L_b is clamped to
+ * [0, max_seq_len]).
+ *
+ * Layouts (device memory, borrowed, 16-byte aligned):
+ *   q_nope, q_pe, kv_cache, block_table, seq_lens, out as for mla_decode_run,
+ *            with any q_tokens in [1, max_seq_len]
+ *   w_uk, w_uv  W_UK and W_UV ([128, 128, 512] each, viewed as 16384 x 512)
+ *            packed by mla_pack_weight
+ * Workspace (mla_naive_workspace_size bytes, 256-byte aligned): the
+ * materialised keys and values, B * ceil(max_seq_len / 64) tiles of 4,104 KiB
+ * (K_nope in bf16, V in fp16, k_R once per tile), i.e. 64 KiB + 128 B per
+ * token against the latent cache's 1,152 B.
+ * Numerics: K_nope and V are rounded once (bf16, fp16) from fp32 sums;
+ * q . K on bf16 matrix cores, the softmax in fp32, P in fp16 against V on fp16
+ * matrix cores, fp32 accumulation. |V| must stay within fp16's range (65504).
+ * Two kernels on `stream`, no allocation, no synchronisation. Errors as for
+ * mla_decode_run. */
+typedef struct mla_naive_args {
+  const void* q_nope;          /* bf16 [B, Sq, 128, 128] */
+  const void* q_pe;            /* bf16 [B, Sq, 128, 64] */
+  const void* w_uk;            /* packed W_UK, 16384 x 512 */
+  const void* w_uv;            /* packed W_UV, 16384 x 512 */
+  const void* kv_cache;        /* bf16 [num_blocks, 64, 576] */
+  const int32_t* block_table;  /* int32 [B, max_blocks_per_seq] */
+  const int32_t* seq_lens;     /* int32 [B] */
+  float* out;                  /* fp32 [B, Sq, 128, 128] */
+  int64_t num_blocks;
+  int32_t batch;               /* 1 <= B <= 1000000 */
+  int32_t q_tokens;            /* 1 <= Sq <= max_seq_len */
+  int32_t max_blocks_per_seq;  /* >= ceil(max_seq_len / 64) */
+  int32_t max_seq_len;         /* 1 <= max_seq_len <= 2^20, bounds every L_b */
+} mla_naive_args;
+
+int mla_naive_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t max_seq_len, size_t* bytes);
+
+int mla_naive_run(const mla_decode_ctx* ctx, const mla_naive_args* args, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* Release a context (NULL is accepted). */
 void mla_decode_destroy(mla_decode_ctx* ctx);
 

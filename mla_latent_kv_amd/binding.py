@@ -89,6 +89,24 @@ class MlaOprojArgs(ctypes.Structure):
     ]
 
 
+class MlaNaiveArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_nope", ctypes.c_void_p),
+        ("q_pe", ctypes.c_void_p),
+        ("w_uk", ctypes.c_void_p),
+        ("w_uv", ctypes.c_void_p),
+        ("kv_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("batch", ctypes.c_int32),
+        ("q_tokens", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -136,6 +154,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_pack_weight.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p]
     lib.mla_pack_weight.restype = ctypes.c_int
+    lib.mla_naive_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_naive_workspace_size.restype = ctypes.c_int
+    lib.mla_naive_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaNaiveArgs), ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_naive_run.restype = ctypes.c_int
     lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
     lib.mla_decode_destroy.restype = None
     lib.mla_decode_status_string.argtypes = [ctypes.c_int]
@@ -397,6 +421,51 @@ def mla_output_project(ctx, x, w_o, y=None, workspace=None, stream=None):
     return y
 
 
+def mla_naive_workspace_size(ctx, batch: int, max_seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mla_naive_workspace_size(ctx, int(batch), int(max_seq_len), ctypes.byref(n)),
+           "mla_naive_workspace_size")
+    return n.value
+
+
+def mla_naive_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_lens,
+                  max_seq_len: int, out=None, workspace=None, stream=None):
+    """Enqueue the naive path (materialised K and V, then causal softmax
+    attention); any Sq in [1, max_seq_len] (Sq = L: prefill). w_uk / w_uv are
+    W_UK / W_UV packed by mla_pack_weight. Returns ``out`` (fp32 [B, Sq, 128, 128])."""
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _require(q_nope, "q_nope", b16, 4)
+    _require(q_pe, "q_pe", b16, 4)
+    _require_packed(w_uk, "w_uk", N_HEADS * D_NOPE, D_LATENT)
+    _require_packed(w_uv, "w_uv", N_HEADS * D_V, D_LATENT)
+    _require(kv_cache, "kv_cache", b16, 3)
+    _require(block_table, "block_table", (torch.int32,), 2)
+    _require(seq_lens, "seq_lens", (torch.int32,), 1)
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    if tuple(q_nope.shape[2:]) != (N_HEADS, D_NOPE) or tuple(q_pe.shape) != (B, Sq, N_HEADS, D_ROPE):
+        raise ValueError("q_nope / q_pe shapes must be [B, Sq, 128, 128] / [B, Sq, 128, 64]")
+    if tuple(kv_cache.shape[1:]) != (BLOCK, D_LATENT + D_ROPE):
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table / seq_lens batch mismatch")
+    if out is None:
+        out = torch.empty((B, Sq, N_HEADS, D_V), dtype=torch.float32, device=q_nope.device)
+    _require(out, "out", (torch.float32,), 4)
+    if tuple(out.shape) != (B, Sq, N_HEADS, D_V):
+        raise ValueError("out must be [B, Sq, 128, 128] fp32")
+    workspace = _workspace(workspace, mla_naive_workspace_size(ctx, B, max_seq_len), q_nope.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q_nope.device)
+    args = MlaNaiveArgs(q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                        kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                        kv_cache.shape[0], B, Sq, block_table.shape[1], int(max_seq_len))
+    _check(load_library().mla_naive_run(ctx, ctypes.byref(args), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        ctypes.c_void_p(s.cuda_stream)),
+           "mla_naive_run")
+    return out
+
+
 class MLADecoder:
     """Owns a context; ``decoder(...)`` forwards to mla_decode_run."""
 
@@ -414,6 +483,10 @@ class MLADecoder:
     def pack(self, w, **kw):
         """Forwards to mla_pack_weight (a weight in the projections' packed layout)."""
         return mla_pack_weight(self.ctx, w, **kw)
+
+    def naive(self, *args, **kw):
+        """Forwards to mla_naive_run (materialised K and V; prefill when Sq = L)."""
+        return mla_naive_run(self.ctx, *args, **kw)
 
     def append(self, *args, **kw):
         """Forwards to mla_cache_append (the new tokens' cache rows)."""

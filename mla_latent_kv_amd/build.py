@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.hip", "prep.hip", "attn.hip", "merge.hip", "wpack.hip", "append.hip", "oproj.hip", "qproj.hip"]
+SOURCES = ["api.hip", "prep.hip", "attn.hip", "merge.hip", "wpack.hip", "append.hip", "oproj.hip", "qproj.hip", "naive.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

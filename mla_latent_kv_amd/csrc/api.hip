@@ -28,6 +28,8 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int32_t kMaxNaiveLen = 1 << 20;   // tokens per sequence on the naive path
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +281,42 @@ int mla_pack_weight(const mla_decode_ctx* ctx, const void* w, void* packed, int3
   const int status =
       mla::launch_pack_weight((const uint16_t*)w, (uint16_t*)packed, n, k, stream) == hipSuccess ? MLA_OK
                                                                                                  : MLA_ERR_HIP;
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
+}
+
+int mla_naive_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t max_seq_len, size_t* bytes) {
+  if (!ctx || !bytes || batch < 1 || batch > mla::kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxNaiveLen)
+    return MLA_ERR_INVALID_ARG;
+  *bytes = mla::naive_workspace_bytes(batch, max_seq_len);
+  return MLA_OK;
+}
+
+int mla_naive_run(const mla_decode_ctx* ctx, const mla_naive_args* a, void* workspace, size_t workspace_bytes,
+                  void* stream_handle) {
+  if (!ctx || !a || !a->q_nope || !a->q_pe || !a->w_uk || !a->w_uv || !a->kv_cache || !a->block_table ||
+      !a->seq_lens || !a->out)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->batch > mla::kMaxBatch || a->max_seq_len < 1 || a->max_seq_len > kMaxNaiveLen ||
+      a->q_tokens < 1 || a->q_tokens > a->max_seq_len || a->num_blocks < 1 || a->max_blocks_per_seq < 1 ||
+      (long long)a->max_blocks_per_seq * mla::kBlock < a->max_seq_len)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(a->q_nope) || !aligned16(a->q_pe) || !aligned16(a->w_uk) || !aligned16(a->w_uv) ||
+      !aligned16(a->kv_cache) || !aligned16(a->block_table) || !aligned16(a->seq_lens) || !aligned16(a->out))
+    return MLA_ERR_MISALIGNED;
+  const size_t need = mla::naive_workspace_bytes(a->batch, a->max_seq_len);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  const int status =
+      mla::launch_naive((const uint16_t*)a->q_nope, (const uint16_t*)a->q_pe, (const uint16_t*)a->w_uk,
+                        (const uint16_t*)a->w_uv, (const uint16_t*)a->kv_cache, a->block_table, a->seq_lens, a->out,
+                        a->num_blocks, a->batch, a->q_tokens, a->max_blocks_per_seq, a->max_seq_len,
+                        ctx->scale, workspace, stream) == hipSuccess
+          ? MLA_OK
+          : MLA_ERR_HIP;
   if (prev != ctx->device) (void)hipSetDevice(prev);
   return status;
 }

@@ -133,6 +133,14 @@ hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_kv, uint16_t*
                          const int32_t* block_table, const int32_t* seq_lens, long long num_blocks,
                          int max_blocks_per_seq, int batch, int q_tokens, double rope_base, void* ws,
                          hipStream_t stream);
+// naive path (two launches): per-head K, V materialised into the workspace
+// (naive_workspace_bytes), then causal softmax attention over them
+size_t naive_workspace_bytes(int batch, int max_len);
+hipError_t launch_naive(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk, const uint16_t* w_uv,
+                        const uint16_t* cache, const int32_t* block_table, const int32_t* seq_lens, float* out,
+                        long long num_blocks, int batch, int q_tokens, int max_blocks_per_seq, int max_len,
+                        float scale, void* ws, hipStream_t stream);
+
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const SeqInfo* seqinfo,
                         const uint16_t* w_uv, float* out, int batch, int q_tokens,
                         hipStream_t stream);

@@ -1,0 +1,506 @@
+// Naive-path attention: the per-head keys and values are materialised from the
+// latent cache,
+//   K_h[j] = [W_UK[h] c_j ; k_R,j]  (192 wide),   V_h[j] = W_UV[h] c_j  (128),
+// and a standard causal softmax attention runs over them, out[b,i,h] =
+// softmax(scale * q_h K_h^T) V_h with row i seeing positions
+// j <= L_b - Sq + i. This is the branch the "DeepSeek-V3" page
+// (ailearn.mscapital.top, MLA paragraphs) contrasts with the absorb order: it
+// expands every cached token to 128 x (192 + 128) = 40,960 elements instead
+// of keeping 576 ("DeepSeek-V3" article at m.lsln.cn, section 2.1: the
+// attention softmax(Q K^T) V over the cached keys and values). With every
+// prompt token as a query (Sq = L, prefill) the work is quadratic in L and
+// bound by the matrix cores.
+//
+// Two launches:
+//  1. expand_kernel, workgroup = 128 tokens of one sequence x one head:
+//     C (128 x 512, bf16) is fetched into LDS, W_UK[h] and W_UV[h] stream
+//     from their packed layout (wstream.h) into registers, and
+//       K_nope[token][n] = C W_UK[h]^T   (MFMA: A = C rows, B = W_UK rows)
+//       V^T[v][token]    = W_UV[h] C^T   (MFMA: A = W_UV rows, B = C rows)
+//     (the same C fragments serve both). Results are rounded (K_nope to bf16,
+//     V to fp16) and written per 64-token tile in the fragment order the
+//     attention pass loads; the head-shared k_R is copied once per tile (by
+//     the head-0 workgroups). Tokens at or past L are written as zeros.
+//  2. attend_kernel, workgroup = 256 queries of one sequence x one head (64
+//     per wavefront): per 64-key tile, one barrier, the next tile's 40 KB
+//     fetched straight into LDS while this one is used; S^T = K Q^T on bf16
+//     MFMA (lane = query, so every query's softmax state stays in its lane
+//     pair), online softmax in fp32, P rounded to fp16 and O^T += V^T P^T on
+//     fp16 MFMA. Causal masking only in the tiles that cross the diagonal.
+//
+// Expanded buffer, per sequence b and 64-token tile j (kTileBytes):
+//   [k_R: 8 fragments][head 0: K 16 fragments | V^T 16 fragments][head 1 ...]
+// Fragment = 1 KB, lane piece l (16 bytes) at 16 l:
+//   K   (kt, s), kt < 2, s < 8:  bf16 K_nope[32 kt + l%32][16 s + 8 (l/32) .. + 7]
+//   k_R (kt, s), kt < 2, s < 4:  bf16 k_R[32 kt + l%32][16 s + 8 (l/32) .. + 7]
+//   V^T (vt, g), vt < 4, g < 4:  fp16 V[t][32 vt + l%32] for the 8 tokens
+//        t = 16 g + 4 (l/32) + {0,1,2,3} and 16 g + 8 + 4 (l/32) + {0,1,2,3}
+// (the token order of V^T matches the accumulator layout of S^T, so the
+// probabilities feed the P V product without a shuffle).
+#include "common.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kNThreads = 256;
+constexpr int kFrag = 1024;
+constexpr int kRFrags = 8, kKFrags = 16, kVFrags = 16;
+constexpr size_t kHeadTileBytes = (size_t)(kKFrags + kVFrags) * kFrag;            // 32 KB
+constexpr size_t kRTileBytes = (size_t)kRFrags * kFrag;                            // 8 KB
+constexpr size_t kTileBytes = kRTileBytes + (size_t)kHeads * kHeadTileBytes;       // per (b, 64 tokens)
+constexpr int kExpTok = 128;                      // tokens per expansion workgroup
+constexpr int kQPerWg = 256;                      // queries per attention workgroup
+constexpr int kPackedTiles = kHeads * kDNope / 32;   // 512 column tiles of the packed W_UK / W_UV
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// One direct-to-LDS fetch: 64 lanes x 16 bytes from base + voff (per lane) to
+// LDS bytes [lds, lds + 1024). Inline asm so that the compiler does not drain
+// it before every LDS read; the kernels order it with explicit waits and
+// barriers. No VGPR result.
+__device__ __forceinline__ void dma16(const char* lds, const char* base, unsigned voff) {
+  const unsigned m0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(base)
+               : "m0");
+}
+
+// Max and sum of x over the lane pair (l, l ^ 32): v_permlane32_swap with
+// both operands x hands each lane its own and its partner's value (the second
+// copy passes an empty asm so the optimizer sees two values). Each element is
+// converted to a scalar before its bit cast (a bit cast applied directly to a
+// vector element reads element 0 with this compiler).
+struct PairF {
+  float a, b;
+};
+__device__ __forceinline__ PairF with_partner(float x) {
+  float y = x;
+  asm volatile("" : "+v"(y));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return PairF{__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
+}
+__device__ __forceinline__ float pair_max(float x) {
+  const PairF p = with_partner(x);
+  return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const PairF p = with_partner(x);
+  return p.a + p.b;
+}
+
+__device__ __forceinline__ unsigned short bf16_rne(float x) {
+  unsigned int u = __builtin_bit_cast(unsigned int, x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// ---------------------------------------------------------------- expansion
+
+struct ExpandArgs {
+  const uint16_t* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const u32x4* w_uk;   // packed W_UK, [16384][512]
+  const u32x4* w_uv;   // packed W_UV, [16384][512]
+  char* exp;
+  long long num_blocks;
+  int max_blocks_per_seq;
+  int t64;             // 64-token tiles per sequence in the expanded buffer
+  int max_len;
+};
+
+constexpr int kCRow = kDLat * 2;                 // 1024 bytes of c_KV per token in LDS
+constexpr int kEpiStride = 136;                  // LDS row of the epilogue tiles: 128 + 8 halves
+
+__device__ __forceinline__ const char* token_row(const ExpandArgs& a, int b, int t) {
+  long long blk = a.block_table[(size_t)b * a.max_blocks_per_seq + t / kBlock];
+  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);   // memory safety
+  return (const char*)(a.cache + ((size_t)blk * kBlock + t % kBlock) * kRow);
+}
+
+// The expansion product of one wavefront over the 32 k-steps of the latent:
+// kV: acc[tt][j] = W_UV rows (column tile j) x C rows (token tile tt), i.e.
+// D[v][token]; else acc[tt][j] = C rows x W_UK rows, D[token][n]. Weight
+// fragments stream from the packed layout through a 4-deep register ring; C
+// fragments come from LDS (row r's piece p at p ^ (r % 64)).
+template <bool kV>
+__device__ __forceinline__ void expand_gemm(const char* smem, const u32x4* wp, f32x16 (&acc)[4][2]) {
+  const int lane = threadIdx.x & 63, n = lane & 31, half = lane >> 5;
+  constexpr int kSteps = kDLat / 16;   // 32
+  constexpr int kDepth = 4;
+  u32x4 wf[kDepth][2];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wf[d][j] = wp[(size_t)d * kPackedTiles * 64 + 64 * j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  for (int k0 = 0; k0 < kSteps; k0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int ks = k0 + d;
+      bf16x8 cf[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int r = 32 * tt + n;
+        cf[tt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + r * kCRow + 16 * ((2 * ks + half) ^ (r & 63))));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 wv = __builtin_bit_cast(bf16x8, wf[d][j]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[tt][j] = kV ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, cf[tt], acc[tt][j], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[tt], wv, acc[tt][j], 0, 0, 0);
+      }
+      const int nk = ks + kDepth < kSteps ? ks + kDepth : kSteps - 1;   // past the end: reload the last
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wf[d][j] = wp[(size_t)nk * kPackedTiles * 64 + 64 * j];
+    }
+  }
+}
+
+// grid (ceil(max_len / 128), 128 heads, B)
+__global__ __launch_bounds__(kNThreads, 1) void expand_kernel(ExpandArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kExpTok * kCRow];   // 128 KB
+  const int b = blockIdx.z, h = blockIdx.y, t0 = blockIdx.x * kExpTok;
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);
+  if (t0 >= L) return;   // tiles at or past L are never read
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n = lane & 31, half = lane >> 5;
+
+  // 1. C rows into LDS: row r holds token t0 + r; 16-byte piece p of the row
+  // sits at p ^ (r % 64) (conflict-free fragment reads). Rows past L fetch
+  // token 0 (a valid row): their results are replaced by zeros below.
+  for (int i = 0; i < 32; ++i) {
+    const int r = 32 * w + i;
+    const int tok = t0 + r < L ? t0 + r : 0;
+    dma16(smem + r * kCRow, token_row(a, b, tok), (unsigned)(16 * (lane ^ (r & 63))));
+  }
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's C rows are in
+  __syncthreads();                                   // ... and everyone's
+
+  // 2. GEMM. Waves 0, 1: K_nope columns [64 w, 64 w + 64); waves 2, 3: V rows
+  // [64 (w - 2), + 64). Each: 4 token tiles x 2 column tiles of 32x32.
+  const bool is_v = w >= 2;
+  const int ct0 = 4 * h + 2 * (w & 1);                      // first packed column tile
+  const u32x4* wp = (is_v ? a.w_uv : a.w_uk) + (size_t)ct0 * 64 + lane;
+  f32x16 acc[4][2];
+  if (is_v)
+    expand_gemm<true>(smem, wp, acc);
+  else
+    expand_gemm<false>(smem, wp, acc);
+  __syncthreads();   // every wave is done with the C rows
+
+  // 3. Rounded results into LDS: K region [token][n] bf16, V region [v][token]
+  // fp16, rows of kEpiStride halves.
+  uint16_t* ek = (uint16_t*)smem;
+  _Float16* ev = (_Float16*)(smem + kExpTok * kEpiStride * 2);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * tt + 8 * (i >> 2) + 4 * half + (i & 3);   // accumulator row
+        const int col = 64 * (w & 1) + 32 * j + n;
+        if (is_v)   // D[v = 64 (w-2) + 32 j + row'][token]: row' indexes v, lane the token
+          ev[(64 * (w & 1) + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3)) * kEpiStride + 32 * tt + n] =
+              (_Float16)acc[tt][j][i];
+        else        // D[token][n]
+          ek[row * kEpiStride + col] = bf16_rne(acc[tt][j][i]);
+      }
+  __syncthreads();
+
+  // 4. Fragments out. The workgroup's two 64-token tiles; 32 K and 32 V^T
+  // fragments (8 + 8 per wave), plus the 16 k_R fragments for head 0.
+  for (int q = 0; q < 2; ++q) {
+    const int j64 = 2 * blockIdx.x + q;
+    if (64 * j64 >= L) break;
+    char* tile = a.exp + ((size_t)b * a.t64 + j64) * kTileBytes;
+    char* head = tile + kRTileBytes + (size_t)h * kHeadTileBytes;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {   // K fragment (kt, s): wave w takes 4 of the 16
+      const int kf = 4 * w + f, kt = kf >> 3, s = kf & 7;
+      const int tok = 64 * q + 32 * kt + n;
+      u32x4 v = *(const u32x4*)(ek + tok * kEpiStride + 16 * s + 8 * half);
+      if (t0 + tok >= L) v = u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(head + kf * kFrag + 16 * lane) = v;
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {   // V^T fragment (vt, g)
+      const int vf = 4 * w + f, vt = vf >> 2, g = vf & 3;
+      const int v = 32 * vt + n;
+      const int ta = 64 * q + 16 * g + 4 * half;   // tokens ta..ta+3 and ta+8..ta+11
+      const _Float16* src = ev + v * kEpiStride;
+      f16x8_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = t0 + ta + e < L ? src[ta + e] : (_Float16)0.f;
+        o[4 + e] = t0 + ta + 8 + e < L ? src[ta + 8 + e] : (_Float16)0.f;
+      }
+      *(f16x8_t*)(head + (kKFrags + vf) * kFrag + 16 * lane) = o;
+    }
+    if (h == 0) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {   // k_R fragment (kt, s)
+        const int rf = 2 * w + f, kt = rf >> 2, s = rf & 3;
+        const int tok = t0 + 64 * q + 32 * kt + n;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (tok < L) v = *(const u32x4*)(token_row(a, b, tok) + 2 * (kDLat + 16 * s + 8 * half));
+        *(u32x4*)(tile + rf * kFrag + 16 * lane) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- attention
+
+struct AttendArgs {
+  const uint16_t* q_nope;
+  const uint16_t* q_pe;
+  const char* exp;
+  const int32_t* seq_lens;
+  float* out;
+  int q_tokens;
+  int t64;
+  int max_len;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+constexpr int kTileLds = (kRFrags + kKFrags + kVFrags) * kFrag;   // 40 KB per key tile
+
+// Rescaling of the running output is deferred until a row's maximum grows by
+// more than 2^kLazy (in log2 units): until then the probabilities are formed
+// against the older maximum and stay below 2^kLazy, well inside fp16.
+constexpr float kLazy = 8.f;
+
+// One 64-key tile for the wavefront's 64 queries (2 query tiles of 32):
+// S^T = K Q^T (bf16 MFMA, 12 k-steps of 16 dims: 8 of K_nope, 4 of k_R), the
+// online softmax (per lane = query; its 64 keys split over the lane pair),
+// then O^T += V^T P^T (fp16 MFMA, 4 groups of 16 keys). kMasked: the tile
+// crosses some row's last visible key.
+template <bool kMasked>
+__device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2][12], const int (&vis)[2], int nt,
+                                            float scale_log2, float (&m)[2], float (&l)[2],
+                                            f32x16 (&oacc)[4][2]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  // The key fragments of k-step s + 1 are read while step s multiplies; the
+  // scheduling barriers keep the compiler from hoisting every LDS read of the
+  // tile to its top (which would leave no room for the query fragments).
+  auto kfrag = [&](int s, int kt) {
+    const int f = s < 8 ? kRFrags + 8 * kt + s : 4 * kt + (s - 8);
+    return *(const u32x4*)(buf + f * kFrag + 16 * lane);
+  };
+  f32x16 sacc[2][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) sacc[kt][0] = sacc[kt][1] = f32x16{};
+  u32x4 kcur[2] = {kfrag(0, 0), kfrag(0, 1)};
+#pragma unroll
+  for (int s = 0; s < 12; ++s) {
+    u32x4 knext[2];
+    if (s + 1 < 12) {
+      knext[0] = kfrag(s + 1, 0);
+      knext[1] = kfrag(s + 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kcur[kt]),
+                                                               __builtin_bit_cast(bf16x8, qf[qt][s]), sacc[kt][qt],
+                                                               0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < 12) {
+      kcur[0] = knext[0];
+      kcur[1] = knext[1];
+    }
+  }
+  f16x8_t pf[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    if constexpr (kMasked) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kBlock * nt + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > vis[qt]) sacc[kt][qt][r] = -INFINITY;
+        }
+    }
+    float tmax = -INFINITY;   // of the raw scores (the scale is positive)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kt][qt][r]);
+    tmax = pair_max(tmax) * scale_log2;
+    // wave-uniform decision: some row's maximum grew by more than 2^kLazy
+    if (__builtin_amdgcn_ballot_w64(tmax > m[qt] + kLazy) != 0) {
+      const float m_new = fmaxf(m[qt], tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qt] - m_new);
+      m[qt] = m_new;
+      l[qt] *= alpha;
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) oacc[vt][qt] *= alpha;
+    }
+    const float neg_m = m[qt] == -INFINITY ? 0.f : -m[qt];   // a row that sees nothing yet: p = 0
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][r], scale_log2, neg_m));
+        psum += p;
+        pf[qt][2 * kt + (r >> 3)][r & 7] = (_Float16)p;
+      }
+    l[qt] += psum;
+  }
+  // O^T += V^T P^T; the value fragments of group g + 1 are read while group
+  // g multiplies
+  auto vfrag = [&](int g, int vt) { return *(const u32x4*)(buf + (kRFrags + kKFrags + 4 * vt + g) * kFrag + 16 * lane); };
+  u32x4 vcur[4];
+#pragma unroll
+  for (int vt = 0; vt < 4; ++vt) vcur[vt] = vfrag(0, vt);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u32x4 vnext[4];
+    if (g + 1 < 4) {
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) vnext[vt] = vfrag(g + 1, vt);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        oacc[vt][qt] =
+            __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vcur[vt]), pf[qt][g], oacc[vt][qt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < 4) {
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) vcur[vt] = vnext[vt];
+    }
+  }
+}
+
+// grid (ceil(Sq / 256) * 128, 1, B). Workgroup id i runs on XCD i % 8 (the
+// dispatcher's round robin); the mapping below gives each XCD whole heads, all
+// query tiles of a head in consecutive slots, so the head's key and value
+// tiles are re-read from that XCD's L2. Within a head the query tiles run
+// last-first (the causal tail has the most key tiles). Results do not depend
+// on where a workgroup runs.
+__global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileLds];
+  const int nq = gridDim.x / kHeads;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int b = blockIdx.z, h = xcd + 8 * (slot / nq);
+  const int qtile = nq - 1 - slot % nq;
+  const int Sq = a.q_tokens;
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n = lane & 31, half = lane >> 5;
+  const int i0 = kQPerWg * qtile;
+  // the workgroup's last visible key, and the key tiles it needs
+  const int vis_max = L - Sq + min(i0 + kQPerWg - 1, Sq - 1);
+  const int n_tiles = vis_max < 0 ? 0 : vis_max / kBlock + 1;
+  const int mask_from = L - Sq + i0 < 0 ? 0 : (L - Sq + i0 + 1) / kBlock;   // first tile that needs masking
+
+  // queries of this lane: rows i = i0 + 64 w + 32 qt + n
+  int qi[2], vis[2];
+  u32x4 qf[2][12];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    qi[qt] = i0 + 64 * w + 32 * qt + n;
+    vis[qt] = L - Sq + qi[qt];
+    const bool ok = qi[qt] < Sq;
+    const size_t row = ((size_t)b * Sq + (ok ? qi[qt] : 0)) * kHeads + h;
+#pragma unroll
+    for (int s = 0; s < 12; ++s) {
+      u32x4 v = s < 8 ? *(const u32x4*)(a.q_nope + row * kDNope + 16 * s + 8 * half)
+                      : *(const u32x4*)(a.q_pe + row * kDRope + 16 * (s - 8) + 8 * half);
+      qf[qt][s] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const size_t seq_base = (size_t)b * a.t64 * kTileBytes;
+  auto fetch = [&](int nt, char* buf) {   // 10 of the tile's 40 fragments per wave
+#pragma unroll
+    for (int k = 0; k < 10; ++k) {
+      const int f = 10 * w + k;
+      const char* src = a.exp + seq_base + (size_t)nt * kTileBytes +
+                        (f < kRFrags ? (size_t)f * kFrag
+                                     : kRTileBytes + (size_t)h * kHeadTileBytes + (size_t)(f - kRFrags) * kFrag);
+      dma16(buf + f * kFrag, src, (unsigned)(16 * lane));
+    }
+  };
+
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int vt = 0; vt < 4; ++vt) oacc[vt][0] = oacc[vt][1] = f32x16{};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+  // per tile: this tile's fragments are in (own share: vmcnt; everyone's: the
+  // barrier, after which the other buffer is free too), then the next tile's
+  // fetch goes out while this one is used
+  auto next = [&](int nt) -> const char* {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nt + 1 < n_tiles) fetch(nt + 1, smem + ((nt + 1) & 1) * kTileLds);
+    return smem + (nt & 1) * kTileLds;
+  };
+  if (n_tiles > 0) fetch(0, smem);
+  const int n_plain = min(mask_from, n_tiles);   // tiles every row sees whole
+  int nt = 0;
+  for (; nt < n_plain; ++nt) attend_tile<false>(next(nt), qf, vis, nt, a.scale_log2, m, l, oacc);
+  for (; nt < n_tiles; ++nt) attend_tile<true>(next(nt), qf, vis, nt, a.scale_log2, m, l, oacc);
+
+  // out[b, i, h, v] = O / l; a row that sees no position yields zeros
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = pair_sum(l[qt]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qi[qt] >= Sq) continue;
+    float* o = a.out + (((size_t)b * Sq + qi[qt]) * kHeads + h) * kDV;
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v = {oacc[vt][qt][4 * g4] * inv, oacc[vt][qt][4 * g4 + 1] * inv, oacc[vt][qt][4 * g4 + 2] * inv,
+                         oacc[vt][qt][4 * g4 + 3] * inv};
+        *(f32x4*)(o + 32 * vt + 8 * g4 + 4 * half) = v;
+      }
+  }
+}
+
+}  // namespace
+
+size_t naive_workspace_bytes(int batch, int max_len) {
+  return (size_t)batch * ((max_len + kBlock - 1) / kBlock) * kTileBytes;
+}
+
+hipError_t launch_naive(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk, const uint16_t* w_uv,
+                        const uint16_t* cache, const int32_t* block_table, const int32_t* seq_lens, float* out,
+                        long long num_blocks, int batch, int q_tokens, int max_blocks_per_seq, int max_len,
+                        float scale, void* ws, hipStream_t stream) {
+  const int t64 = (max_len + kBlock - 1) / kBlock;
+  const ExpandArgs ea{cache, block_table, seq_lens, (const u32x4*)w_uk, (const u32x4*)w_uv, (char*)ws,
+                      num_blocks, max_blocks_per_seq, t64, max_len};
+  hipLaunchKernelGGL(expand_kernel, dim3((max_len + kExpTok - 1) / kExpTok, kHeads, batch), dim3(kNThreads), 0,
+                     stream, ea);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const AttendArgs aa{q_nope, q_pe, (const char*)ws, seq_lens, out, q_tokens, t64, max_len,
+                      scale * 1.4426950408889634f};
+  static_assert(kHeads % 8 == 0, "whole heads per XCD");
+  hipLaunchKernelGGL(attend_kernel, dim3((q_tokens + kQPerWg - 1) / kQPerWg * kHeads, 1, batch), dim3(kNThreads), 0,
+                     stream, aa);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported():
                         "mla_decode_status_string", "mla_cache_append",
                         "mla_cache_append_workspace_size", "mla_output_project",
                         "mla_output_project_workspace_size", "mla_query_project",
-                        "mla_query_project_workspace_size", "mla_pack_weight"}
+                        "mla_query_project_workspace_size", "mla_pack_weight",
+                        "mla_naive_workspace_size", "mla_naive_run"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -117,3 +118,14 @@ def test_query_project_rejects_nulls_before_any_device_call():
     assert lib.mla_query_project_workspace_size(None, 4, 1, ctypes.byref(n)) == -1
     args = binding.MlaQueryArgs()
     assert lib.mla_query_project(None, ctypes.byref(args), None, 0, None) == -1
+
+
+def test_naive_rejects_nulls_before_any_device_call():
+    import ctypes
+    from mla_latent_kv_amd import binding
+    lib = _lib()
+    n = ctypes.c_size_t()
+    assert lib.mla_naive_workspace_size(None, 1, 4096, ctypes.byref(n)) == -1
+    args = binding.MlaNaiveArgs()
+    assert lib.mla_naive_run(None, ctypes.byref(args), None, 0, None) == -1
+    assert lib.mla_naive_run(None, None, None, 0, None) == -1
