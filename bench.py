@@ -45,8 +45,8 @@ QPROJ_WEIGHT_BYTES = (1536 * 7168 + 128 * 192 * 1536) * 2   # W_DQ and W_UQ, bf1
 # the same counter reads for a plain device copy of known size (--copy-probe).
 # The figures belong to the attention source they were taken on: when the
 # source hash differs, traffic is reported as null.
-ATTN_TRAFFIC = {"src_sha256": "85b986fef3590bab81fe984abb669ef6b5326b254ce1f558743ab3d6ee76cf73",
-                "fetch_kib": 76215.277, "write_kib": 32896.0,
+ATTN_TRAFFIC = {"src_sha256": "c952efa6f52f6c011759083ed552a4483b7bc3ba06ea616f79b8ddc0d328f38a",
+                "fetch_kib": 76215.167, "write_kib": 32896.0,
                 "fetch_scale": 1.99995, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
 
@@ -302,6 +302,76 @@ def time_query_project(lib, dec, d, B, Sq, stream, args) -> dict:
     return out
 
 
+PREFILL_SPEC = ("prefill_b1_l4096", 1, 4096)   # one 4096-token prompt, every token a query
+
+
+def time_naive(lib, dec, d, B, Sq, stream, args, absorb_ms) -> dict:
+    """The naive path (mla_naive_run: per-head K and V materialised, then
+    causal softmax attention). Prefill of one 4096-token prompt (all 128 heads,
+    matrix-core bound: measured against the bf16/fp16 MFMA peak), and the same
+    path on this decode workload beside the absorbed step (the absorb win).
+    HIP events around the calls on the launch stream."""
+    import torch
+    from mla_latent_kv_amd import binding, device, synth
+    name, pb, L = PREFILL_SPEC
+    pbatch = synth.make_batch(synth.Spec(name, pb, L, ("fixed", L)), seed=5000)
+    pd = device.upload(pbatch)
+    w_uk, w_uv = dec.pack(pd["w_uk"]), dec.pack(pd["w_uv"])
+    pws = torch.empty(binding.mla_naive_workspace_size(dec.ctx, pb, L), dtype=torch.uint8, device="cuda")
+    pout = torch.empty((pb, L, 128, 128), dtype=torch.float32, device="cuda")
+
+    def prefill():
+        dec.naive(pd["q_nope"], pd["q_pe"], w_uk, w_uv, pd["kv_cache"], pd["block_table"], pd["seq_lens"],
+                  L, out=pout, workspace=pws, stream=stream)
+
+    def timed(fn, warm, n):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    us = timed(prefill, 2, 10)
+    attn_flop = pb * sum(i + 1 for i in range(L)) * 128 * (192 + 128) * 2   # causal: row i sees i + 1 keys
+    exp_flop = pb * L * 128 * (128 + 128) * 512 * 2                            # K_nope and V from c_KV
+    tflops = (attn_flop + exp_flop) / (us * 1e-6) / 1e12
+    out = {"prefill": {"workload": name, "prompt_tokens": pb * L, "us_per_call": us,
+                       "prompt_tokens_per_s": pb * L / (us * 1e-6), "algorithmic_TFLOP": (attn_flop + exp_flop) / 1e12,
+                       "TFLOPs": tflops, "mfma_frac": tflops / MFMA_PEAK_TFLOPS, "launches": 2,
+                       "expanded_bytes_per_token": 128 * 256 * 2 + 128, "latent_bytes_per_token": 1152}}
+    del pws, pout
+    torch.cuda.empty_cache()
+    # the decode workload on the naive path
+    w_uk, w_uv = dec.pack(d["w_uk"]), dec.pack(d["w_uv"])
+    dws = torch.empty(binding.mla_naive_workspace_size(dec.ctx, B, d["max_seq_len"]), dtype=torch.uint8,
+                      device="cuda")
+    dout = torch.empty((B, Sq, 128, 128), dtype=torch.float32, device="cuda")
+
+    def naive_decode():
+        dec.naive(d["q_nope"], d["q_pe"], w_uk, w_uv, d["kv_cache"], d["block_table"], d["seq_lens"],
+                  d["max_seq_len"], out=dout, workspace=dws, stream=stream)
+
+    nus = timed(naive_decode, 1, 3)
+    out["decode_naive"] = {"us_per_call": nus, "absorb_us_per_step": absorb_ms * 1e3,
+                           "absorb_speedup": nus / (absorb_ms * 1e3), "workspace_GB": dws.numel() / 1e9}
+    del dws, dout
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        # the oracle's naive path on one head of the prompt, scaled to 128 heads
+        from oracle import mla_oracle as orc
+        t0 = time.perf_counter()
+        orc.decode_batch(pbatch["q_nope"], pbatch["q_pe"], pbatch["w_uk"], pbatch["w_uv"], pbatch["cache"],
+                         pbatch["block_table"], pbatch["seq_lens"], 64, sample=[(0, 0)])
+        out["prefill"]["cpu_oracle_us_per_call"] = (time.perf_counter() - t0) * 1e6 * 128
+        out["prefill"]["cpu_oracle_sample"] = "1 of 128 heads, scaled by 128"
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,8 +382,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-append", action="store_true",
-                    help="skip the timings of the cache-append producer, the query side and the "
-                         "output projection")
+                    help="skip the timings of the cache-append producer, the query side, the "
+                         "output projection and the naive path")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -448,6 +518,7 @@ def main() -> int:
         result["cache_append"] = time_cache_append(lib, dec, d, B, Sq, stream, args)
         result["query_project"] = time_query_project(lib, dec, d, B, Sq, stream, args)
         result["output_project"] = time_output_project(lib, dec, B, Sq, stream, args)
+        result["naive"] = time_naive(lib, dec, d, B, Sq, stream, args, ms)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0])
     print(json.dumps(result), flush=True)
