@@ -12,15 +12,19 @@
 // bound by the matrix cores.
 //
 // Two launches:
-//  1. expand_kernel, workgroup = 128 tokens of one sequence x one head:
-//     C (128 x 512, bf16) is fetched into LDS, W_UK[h] and W_UV[h] stream
-//     from their packed layout (wstream.h) into registers, and
-//       K_nope[token][n] = C W_UK[h]^T   (MFMA: A = C rows, B = W_UK rows)
-//       V^T[v][token]    = W_UV[h] C^T   (MFMA: A = W_UV rows, B = C rows)
-//     (the same C fragments serve both). Results are rounded (K_nope to bf16,
-//     V to fp16) and written per 64-token tile in the fragment order the
-//     attention pass loads; the head-shared k_R is copied once per tile (by
-//     the head-0 workgroups). Tokens at or past L are written as zeros.
+//  1. expand_kernel, workgroup = one head x a range of 64-token tiles of one
+//     sequence, 4 wavefronts of 64 output columns: each holds its columns of
+//     W_UK[h] (2 wavefronts) or W_UV[h] (2) in registers, loaded once from
+//     the packed layout (wstream.h), while the tiles' c_KV rows stream
+//     through a 2-deep LDS ring:
+//       K_nope^T[n][token] = W_UK[h] C^T  (MFMA: A = W_UK rows, B = C rows)
+//       V[token][v]        = C W_UV[h]^T  (MFMA: A = C rows, B = W_UV rows)
+//     In both the accumulator of a lane already holds one fragment of the
+//     attention pass (lane = token for K, lane = v for V^T), so each result
+//     is rounded (K_nope to bf16, V to fp16) and stored straight from the
+//     registers as whole 1 KB fragments. The head-shared k_R is copied once
+//     per tile (by the head-0 workgroups). Tokens at or past L are written as
+//     zeros.
 //  2. attend_kernel, workgroup = 256 queries of one sequence x one head (64
 //     per wavefront): per 64-key tile, one barrier, the next tile's 40 KB
 //     fetched straight into LDS while this one is used; S^T = K Q^T on bf16
@@ -31,7 +35,10 @@
 // Expanded buffer, per sequence b and 64-token tile j (kTileBytes):
 //   [k_R: 8 fragments][head 0: K 16 fragments | V^T 16 fragments][head 1 ...]
 // Fragment = 1 KB, lane piece l (16 bytes) at 16 l:
-//   K   (kt, s), kt < 2, s < 8:  bf16 K_nope[32 kt + l%32][16 s + 8 (l/32) .. + 7]
+//   K   (kt, s), kt < 2, s < 8:  bf16 K_nope[32 kt + l%32][16 s + n(e)], e < 8,
+//        n(e) = 4 (l/32) + e for e < 4 and 8 + 4 (l/32) + e - 4 after: a
+//        permutation of the step's 16 dims (the query fragments take the
+//        same one; a dot product does not depend on the order of its terms)
 //   k_R (kt, s), kt < 2, s < 4:  bf16 k_R[32 kt + l%32][16 s + 8 (l/32) .. + 7]
 //   V^T (vt, g), vt < 4, g < 4:  fp16 V[t][32 vt + l%32] for the 8 tokens
 //        t = 16 g + 4 (l/32) + {0,1,2,3} and 16 g + 8 + 4 (l/32) + {0,1,2,3}
@@ -49,7 +56,6 @@ constexpr int kRFrags = 8, kKFrags = 16, kVFrags = 16;
 constexpr size_t kHeadTileBytes = (size_t)(kKFrags + kVFrags) * kFrag;            // 32 KB
 constexpr size_t kRTileBytes = (size_t)kRFrags * kFrag;                            // 8 KB
 constexpr size_t kTileBytes = kRTileBytes + (size_t)kHeads * kHeadTileBytes;       // per (b, 64 tokens)
-constexpr int kExpTok = 128;                      // tokens per expansion workgroup
 constexpr int kQPerWg = 256;                      // queries per attention workgroup
 constexpr int kPackedTiles = kHeads * kDNope / 32;   // 512 column tiles of the packed W_UK / W_UV
 
@@ -113,146 +119,154 @@ struct ExpandArgs {
   int max_len;
 };
 
+constexpr int kXThreads = 256;                   // 4 wavefronts: 64 output columns each
 constexpr int kCRow = kDLat * 2;                 // 1024 bytes of c_KV per token in LDS
-constexpr int kEpiStride = 136;                  // LDS row of the epilogue tiles: 128 + 8 halves
+constexpr int kCTile = kBlock * kCRow;           // 64 KB: the c_KV of one 64-token tile
+constexpr int kLatSteps = kDLat / 16;            // 32 k-steps over the latent
 
-__device__ __forceinline__ const char* token_row(const ExpandArgs& a, int b, int t) {
-  long long blk = a.block_table[(size_t)b * a.max_blocks_per_seq + t / kBlock];
-  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);   // memory safety
-  return (const char*)(a.cache + ((size_t)blk * kBlock + t % kBlock) * kRow);
+__device__ __forceinline__ long long clamp_block(const ExpandArgs& a, int b, int j) {
+  const long long blk = a.block_table[(size_t)b * a.max_blocks_per_seq + j];
+  return blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);   // memory safety
 }
 
-// The expansion product of one wavefront over the 32 k-steps of the latent:
-// kV: acc[tt][j] = W_UV rows (column tile j) x C rows (token tile tt), i.e.
-// D[v][token]; else acc[tt][j] = C rows x W_UK rows, D[token][n]. Weight
-// fragments stream from the packed layout through a 4-deep register ring; C
-// fragments come from LDS (row r's piece p at p ^ (r % 64)).
+// One 64-token tile of one head for a wavefront: 32 k-steps x 2 token tiles
+// x 2 column tiles. kV: D[token][v] = C rows x W_UV rows -- lane = v, the
+// accumulator runs over tokens, which is the V^T fragment order. Else
+// D[n][token] = W_UK rows x C rows -- lane = token, the accumulator runs over
+// n, which is the K fragment order with the n order of each 16-wide k-step
+// permuted (see K_nope above). The weight fragments wf stay in registers for
+// the whole workgroup; C fragments come from LDS (row r's piece p at
+// p ^ (r % 64)), each used for both column tiles.
 template <bool kV>
-__device__ __forceinline__ void expand_gemm(const char* smem, const u32x4* wp, f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void expand_tile(const char* buf, const u32x4 (&wf)[kLatSteps][2],
+                                            f32x16 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, n = lane & 31, half = lane >> 5;
-  constexpr int kSteps = kDLat / 16;   // 32
-  constexpr int kDepth = 4;
-  u32x4 wf[kDepth][2];
+  auto cfrag = [&](int ks, int tt) {
+    const int r = 32 * tt + n;
+    return *(const u32x4*)(buf + r * kCRow + 16 * ((2 * ks + half) ^ (r & 63)));
+  };
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
+  for (int tt = 0; tt < 2; ++tt) acc[tt][0] = acc[tt][1] = f32x16{};
+  // the C fragments of k-step ks + 1 are read while step ks multiplies; the
+  // scheduling barriers keep the reads from all being hoisted to the top
+  u32x4 cur[2] = {cfrag(0, 0), cfrag(0, 1)};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wf[d][j] = wp[(size_t)d * kPackedTiles * 64 + 64 * j];
+  for (int ks = 0; ks < kLatSteps; ++ks) {
+    u32x4 nxt[2];
+    if (ks + 1 < kLatSteps) {
+      nxt[0] = cfrag(ks + 1, 0);
+      nxt[1] = cfrag(ks + 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16{};
-  for (int k0 = 0; k0 < kSteps; k0 += kDepth) {
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int ks = k0 + d;
-      bf16x8 cf[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int r = 32 * tt + n;
-        cf[tt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + r * kCRow + 16 * ((2 * ks + half) ^ (r & 63))));
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 cf = __builtin_bit_cast(bf16x8, cur[tt]);
+        const bf16x8 wv = __builtin_bit_cast(bf16x8, wf[ks][c]);
+        acc[tt][c] = kV ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, wv, acc[tt][c], 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, cf, acc[tt][c], 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 wv = __builtin_bit_cast(bf16x8, wf[d][j]);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          acc[tt][j] = kV ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, cf[tt], acc[tt][j], 0, 0, 0)
-                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[tt], wv, acc[tt][j], 0, 0, 0);
-      }
-      const int nk = ks + kDepth < kSteps ? ks + kDepth : kSteps - 1;   // past the end: reload the last
-#pragma unroll
-      for (int j = 0; j < 2; ++j) wf[d][j] = wp[(size_t)nk * kPackedTiles * 64 + 64 * j];
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks + 1 < kLatSteps) {
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
     }
   }
 }
 
-// grid (ceil(max_len / 128), 128 heads, B)
-__global__ __launch_bounds__(kNThreads, 1) void expand_kernel(ExpandArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kExpTok * kCRow];   // 128 KB
-  const int b = blockIdx.z, h = blockIdx.y, t0 = blockIdx.x * kExpTok;
+// grid (token splits, 128 heads, B). Workgroup (s, h, b) covers the 64-token
+// tiles [j0, j1) of sequence b for head h: wavefront w loads its 64 columns
+// of W_UK[h] (w < 2) or W_UV[h] (w >= 2) once (64 fragments, 256 registers),
+// then the tiles' c_KV rows stream through a 2-deep LDS ring (direct-to-LDS
+// fetches, the next tile in flight while this one multiplies) and every
+// wavefront writes its 8 fragments of the tile straight from its
+// accumulators.
+__global__ __launch_bounds__(kXThreads, 1) void expand_kernel(ExpandArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kCTile];   // 128 KB
+  const int b = blockIdx.z, h = blockIdx.y;
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
-  if (t0 >= L) return;   // tiles at or past L are never read
+  const int T = (L + kBlock - 1) / kBlock;
+  const int j0 = (int)((long long)T * blockIdx.x / gridDim.x), j1 = (int)((long long)T * (blockIdx.x + 1) / gridDim.x);
+  if (j0 >= j1) return;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n = lane & 31, half = lane >> 5;
-
-  // 1. C rows into LDS: row r holds token t0 + r; 16-byte piece p of the row
-  // sits at p ^ (r % 64) (conflict-free fragment reads). Rows past L fetch
-  // token 0 (a valid row): their results are replaced by zeros below.
-  for (int i = 0; i < 32; ++i) {
-    const int r = 32 * w + i;
-    const int tok = t0 + r < L ? t0 + r : 0;
-    dma16(smem + r * kCRow, token_row(a, b, tok), (unsigned)(16 * (lane ^ (r & 63))));
-  }
-
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's C rows are in
-  __syncthreads();                                   // ... and everyone's
-
-  // 2. GEMM. Waves 0, 1: K_nope columns [64 w, 64 w + 64); waves 2, 3: V rows
-  // [64 (w - 2), + 64). Each: 4 token tiles x 2 column tiles of 32x32.
   const bool is_v = w >= 2;
-  const int ct0 = 4 * h + 2 * (w & 1);                      // first packed column tile
-  const u32x4* wp = (is_v ? a.w_uv : a.w_uk) + (size_t)ct0 * 64 + lane;
-  f32x16 acc[4][2];
-  if (is_v)
-    expand_gemm<true>(smem, wp, acc);
-  else
-    expand_gemm<false>(smem, wp, acc);
-  __syncthreads();   // every wave is done with the C rows
+  const int c0 = 2 * (w & 1);        // first of the wavefront's two column tiles within the head
+  const u32x4* wp = (is_v ? a.w_uv : a.w_uk) + (size_t)(4 * h + c0) * 64 + lane;
+  u32x4 wf[kLatSteps][2];
+#pragma unroll
+  for (int ks = 0; ks < kLatSteps; ++ks)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) wf[ks][c] = wp[(size_t)ks * kPackedTiles * 64 + 64 * c];
 
-  // 3. Rounded results into LDS: K region [token][n] bf16, V region [v][token]
-  // fp16, rows of kEpiStride halves.
-  uint16_t* ek = (uint16_t*)smem;
-  _Float16* ev = (_Float16*)(smem + kExpTok * kEpiStride * 2);
+  auto fetch = [&](int j, char* buf) {   // rows 16 w .. 16 w + 15 of tile j
+    const char* blk = (const char*)(a.cache + (size_t)clamp_block(a, b, j) * kBlock * kRow);
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * tt + 8 * (i >> 2) + 4 * half + (i & 3);   // accumulator row
-        const int col = 64 * (w & 1) + 32 * j + n;
-        if (is_v)   // D[v = 64 (w-2) + 32 j + row'][token]: row' indexes v, lane the token
-          ev[(64 * (w & 1) + 32 * j + 8 * (i >> 2) + 4 * half + (i & 3)) * kEpiStride + 32 * tt + n] =
-              (_Float16)acc[tt][j][i];
-        else        // D[token][n]
-          ek[row * kEpiStride + col] = bf16_rne(acc[tt][j][i]);
-      }
-  __syncthreads();
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * w + i;
+      dma16(buf + r * kCRow, blk + (size_t)r * kRow * 2, (unsigned)(16 * (lane ^ (r & 63))));
+    }
+  };
+  fetch(j0, smem);
+  for (int j = j0; j < j1; ++j) {
+    const char* buf = smem + ((j - j0) & 1) * kCTile;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // own share of tile j (and the weights) in
+    __syncthreads();                                   // everyone's; the other buffer is free
+    if (j + 1 < j1) fetch(j + 1, smem + ((j + 1 - j0) & 1) * kCTile);
+    f32x16 acc[2][2];
+    if (is_v)
+      expand_tile<true>(buf, wf, acc);
+    else
+      expand_tile<false>(buf, wf, acc);
 
-  // 4. Fragments out. The workgroup's two 64-token tiles; 32 K and 32 V^T
-  // fragments (8 + 8 per wave), plus the 16 k_R fragments for head 0.
-  for (int q = 0; q < 2; ++q) {
-    const int j64 = 2 * blockIdx.x + q;
-    if (64 * j64 >= L) break;
-    char* tile = a.exp + ((size_t)b * a.t64 + j64) * kTileBytes;
+    char* tile = a.exp + ((size_t)b * a.t64 + j) * kTileBytes;
     char* head = tile + kRTileBytes + (size_t)h * kHeadTileBytes;
+    const int tok0 = kBlock * j;
+    if (!is_v) {
+      // K fragment (kt = tt, s = 2 (c0 + c) + s2): lane (token n, half) takes
+      // acc[tt][c][8 s2 + e] = K_nope[token][16 s + {4 half + e, 8 + 4 half + e - 4}]
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {   // K fragment (kt, s): wave w takes 4 of the 16
-      const int kf = 4 * w + f, kt = kf >> 3, s = kf & 7;
-      const int tok = 64 * q + 32 * kt + n;
-      u32x4 v = *(const u32x4*)(ek + tok * kEpiStride + 16 * s + 8 * half);
-      if (t0 + tok >= L) v = u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)(head + kf * kFrag + 16 * lane) = v;
-    }
+      for (int tt = 0; tt < 2; ++tt) {
+        const bool live = tok0 + 32 * tt + n < L;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {   // V^T fragment (vt, g)
-      const int vf = 4 * w + f, vt = vf >> 2, g = vf & 3;
-      const int v = 32 * vt + n;
-      const int ta = 64 * q + 16 * g + 4 * half;   // tokens ta..ta+3 and ta+8..ta+11
-      const _Float16* src = ev + v * kEpiStride;
-      f16x8_t o;
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] = t0 + ta + e < L ? src[ta + e] : (_Float16)0.f;
-        o[4 + e] = t0 + ta + 8 + e < L ? src[ta + 8 + e] : (_Float16)0.f;
+          for (int s2 = 0; s2 < 2; ++s2) {
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = live ? ((unsigned)bf16_rne(acc[tt][c][8 * s2 + 2 * e]) |
+                             ((unsigned)bf16_rne(acc[tt][c][8 * s2 + 2 * e + 1]) << 16))
+                          : 0u;
+            *(u32x4*)(head + (8 * tt + 2 * (c0 + c) + s2) * kFrag + 16 * lane) = v;
+          }
       }
-      *(f16x8_t*)(head + (kKFrags + vf) * kFrag + 16 * lane) = o;
-    }
-    if (h == 0) {
+    } else {
+      // V^T fragment (vt = c0 + c, g): lane (v n, half) takes acc[g / 2][c][8 (g % 2) + e]
+      // = V[16 g + {4 half + e, 8 + 4 half + e - 4}][v]
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {   // k_R fragment (kt, s)
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f16x8_t o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tok = tok0 + 16 * g + (e < 4 ? 4 * half + e : 8 + 4 * half + (e - 4));
+            o[e] = tok < L ? (_Float16)acc[g >> 1][c][8 * (g & 1) + e] : (_Float16)0.f;
+          }
+          *(f16x8_t*)(head + (kKFrags + 4 * (c0 + c) + g) * kFrag + 16 * lane) = o;
+        }
+    }
+    if (h == 0) {   // k_R fragments (kt, s) of the tile from the cache rows: 2 per wavefront
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
         const int rf = 2 * w + f, kt = rf >> 2, s = rf & 3;
-        const int tok = t0 + 64 * q + 32 * kt + n;
+        const int tok = tok0 + 32 * kt + n;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (tok < L) v = *(const u32x4*)(token_row(a, b, tok) + 2 * (kDLat + 16 * s + 8 * half));
+        if (tok < L)
+          v = *(const u32x4*)((const char*)(a.cache + ((size_t)clamp_block(a, b, j) * kBlock + tok % kBlock) * kRow) +
+                              2 * (kDLat + 16 * s + 8 * half));
         *(u32x4*)(tile + rf * kFrag + 16 * lane) = v;
       }
     }
@@ -346,8 +360,22 @@ __device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qt] - m_new);
       m[qt] = m_new;
       l[qt] *= alpha;
+      // O *= alpha in place in the accumulator registers (read / multiply /
+      // write per element, so O never leaves the AGPRs and the compiler keeps
+      // no VGPR copy of it); the s_nops cover the MFMA -> accumulator-read and
+      // write -> MFMA distances.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt) oacc[vt][qt] *= alpha;
+      for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = oacc[vt][qt][i], tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(x), "=&v"(tmp)
+                       : "v"(alpha));
+          oacc[vt][qt][i] = x;
+        }
+      asm volatile("s_nop 7" ::: "memory");
     }
     const float neg_m = m[qt] == -INFINITY ? 0.f : -m[qt];   // a row that sees nothing yet: p = 0
     float psum = 0.f;
@@ -422,8 +450,14 @@ __global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
     const size_t row = ((size_t)b * Sq + (ok ? qi[qt] : 0)) * kHeads + h;
 #pragma unroll
     for (int s = 0; s < 12; ++s) {
-      u32x4 v = s < 8 ? *(const u32x4*)(a.q_nope + row * kDNope + 16 * s + 8 * half)
-                      : *(const u32x4*)(a.q_pe + row * kDRope + 16 * (s - 8) + 8 * half);
+      u32x4 v;
+      if (s < 8) {   // the K_nope steps' permuted n order: 16 s + {4 half + 0..3, 8 + 4 half + 0..3}
+        const u32x2 lo = *(const u32x2*)(a.q_nope + row * kDNope + 16 * s + 4 * half);
+        const u32x2 hi = *(const u32x2*)(a.q_nope + row * kDNope + 16 * s + 8 + 4 * half);
+        v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        v = *(const u32x4*)(a.q_pe + row * kDRope + 16 * (s - 8) + 8 * half);
+      }
       qf[qt][s] = ok ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -491,8 +525,10 @@ hipError_t launch_naive(const uint16_t* q_nope, const uint16_t* q_pe, const uint
   const int t64 = (max_len + kBlock - 1) / kBlock;
   const ExpandArgs ea{cache, block_table, seq_lens, (const u32x4*)w_uk, (const u32x4*)w_uv, (char*)ws,
                       num_blocks, max_blocks_per_seq, t64, max_len};
-  hipLaunchKernelGGL(expand_kernel, dim3((max_len + kExpTok - 1) / kExpTok, kHeads, batch), dim3(kNThreads), 0,
-                     stream, ea);
+  // enough workgroups for the chip: one per head and sequence, two per head
+  // for a single sequence
+  const int splits = batch == 1 ? 2 : 1;
+  hipLaunchKernelGGL(expand_kernel, dim3(splits, kHeads, batch), dim3(kXThreads), 0, stream, ea);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const AttendArgs aa{q_nope, q_pe, (const char*)ws, seq_lens, out, q_tokens, t64, max_len,

@@ -179,7 +179,7 @@ def test_scan_finds_planted_hazards():
     assert any(h.startswith("R2") for h in scan(late))
 
 
-@pytest.mark.parametrize("src", ["attn.hip", "prep.hip", "merge.hip"])
+@pytest.mark.parametrize("src", ["attn.hip", "prep.hip", "merge.hip", "naive.hip"])
 def test_no_mfma_hazards(src, tmp_path):
     hz = scan(_device_asm(src, tmp_path))
     assert hz == [], "\n".join(hz[:20])
