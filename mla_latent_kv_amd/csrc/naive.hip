@@ -50,7 +50,6 @@ namespace mla {
 
 namespace {
 
-constexpr int kNThreads = 256;
 constexpr int kFrag = 1024;
 constexpr int kRFrags = 8, kKFrags = 16, kVFrags = 16;
 constexpr size_t kHeadTileBytes = (size_t)(kKFrags + kVFrags) * kFrag;            // 32 KB
@@ -288,6 +287,9 @@ struct AttendArgs {
 };
 
 constexpr int kTileLds = (kRFrags + kKFrags + kVFrags) * kFrag;   // 40 KB per key tile
+constexpr int kAQT = 1;                                 // 32-query tiles per wavefront
+constexpr int kAWaves = kQPerWg / (32 * kAQT);         // 8 wavefronts, two per SIMD
+static_assert((kRFrags + kKFrags + kVFrags) % kAWaves == 0, "whole fetch shares");
 
 // Rescaling of the running output is deferred until a row's maximum grows by
 // more than 2^kLazy (in log2 units): until then the probabilities are formed
@@ -299,10 +301,10 @@ constexpr float kLazy = 8.f;
 // online softmax (per lane = query; its 64 keys split over the lane pair),
 // then O^T += V^T P^T (fp16 MFMA, 4 groups of 16 keys). kMasked: the tile
 // crosses some row's last visible key.
-template <bool kMasked>
-__device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2][12], const int (&vis)[2], int nt,
-                                            float scale_log2, float (&m)[2], float (&l)[2],
-                                            f32x16 (&oacc)[4][2]) {
+template <bool kMasked, int kQT>
+__device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[kQT][12], const int (&vis)[kQT],
+                                            int nt, float scale_log2, float (&m)[kQT], float (&l)[kQT],
+                                            f32x16 (&oacc)[4][kQT]) {
   const int lane = threadIdx.x & 63, half = lane >> 5;
   // The key fragments of k-step s + 1 are read while step s multiplies; the
   // scheduling barriers keep the compiler from hoisting every LDS read of the
@@ -311,9 +313,11 @@ __device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2
     const int f = s < 8 ? kRFrags + 8 * kt + s : 4 * kt + (s - 8);
     return *(const u32x4*)(buf + f * kFrag + 16 * lane);
   };
-  f32x16 sacc[2][2];
+  f32x16 sacc[2][kQT];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) sacc[kt][0] = sacc[kt][1] = f32x16{};
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) sacc[kt][qt] = f32x16{};
   u32x4 kcur[2] = {kfrag(0, 0), kfrag(0, 1)};
 #pragma unroll
   for (int s = 0; s < 12; ++s) {
@@ -326,7 +330,7 @@ __device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < kQT; ++qt)
         sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kcur[kt]),
                                                                __builtin_bit_cast(bf16x8, qf[qt][s]), sacc[kt][qt],
                                                                0, 0, 0);
@@ -336,9 +340,9 @@ __device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2
       kcur[1] = knext[1];
     }
   }
-  f16x8_t pf[2][4];
+  f16x8_t pf[kQT][4];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     if constexpr (kMasked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -406,7 +410,7 @@ __device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2
 #pragma unroll
     for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < kQT; ++qt)
         oacc[vt][qt] =
             __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vcur[vt]), pf[qt][g], oacc[vt][qt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -423,7 +427,7 @@ __device__ __forceinline__ void attend_tile(const char* buf, const u32x4 (&qf)[2
 // tiles are re-read from that XCD's L2. Within a head the query tiles run
 // last-first (the causal tail has the most key tiles). Results do not depend
 // on where a workgroup runs.
-__global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kAWaves * 64, 1) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kTileLds];
   const int nq = gridDim.x / kHeads;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
@@ -439,12 +443,12 @@ __global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
   const int n_tiles = vis_max < 0 ? 0 : vis_max / kBlock + 1;
   const int mask_from = L - Sq + i0 < 0 ? 0 : (L - Sq + i0 + 1) / kBlock;   // first tile that needs masking
 
-  // queries of this lane: rows i = i0 + 64 w + 32 qt + n
-  int qi[2], vis[2];
-  u32x4 qf[2][12];
+  // queries of this lane: rows i = i0 + 32 kAQT w + 32 qt + n
+  int qi[kAQT], vis[kAQT];
+  u32x4 qf[kAQT][12];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    qi[qt] = i0 + 64 * w + 32 * qt + n;
+  for (int qt = 0; qt < kAQT; ++qt) {
+    qi[qt] = i0 + 32 * kAQT * w + 32 * qt + n;
     vis[qt] = L - Sq + qi[qt];
     const bool ok = qi[qt] < Sq;
     const size_t row = ((size_t)b * Sq + (ok ? qi[qt] : 0)) * kHeads + h;
@@ -463,10 +467,11 @@ __global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
   }
 
   const size_t seq_base = (size_t)b * a.t64 * kTileBytes;
-  auto fetch = [&](int nt, char* buf) {   // 10 of the tile's 40 fragments per wave
+  constexpr int kFetch = (kRFrags + kKFrags + kVFrags) / kAWaves;   // fragments per wavefront
+  auto fetch = [&](int nt, char* buf) {
 #pragma unroll
-    for (int k = 0; k < 10; ++k) {
-      const int f = 10 * w + k;
+    for (int k = 0; k < kFetch; ++k) {
+      const int f = kFetch * w + k;
       const char* src = a.exp + seq_base + (size_t)nt * kTileBytes +
                         (f < kRFrags ? (size_t)f * kFrag
                                      : kRTileBytes + (size_t)h * kHeadTileBytes + (size_t)(f - kRFrags) * kFrag);
@@ -474,10 +479,15 @@ __global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
     }
   };
 
-  f32x16 oacc[4][2];
+  f32x16 oacc[4][kAQT];
+  float m[kAQT], l[kAQT];
 #pragma unroll
-  for (int vt = 0; vt < 4; ++vt) oacc[vt][0] = oacc[vt][1] = f32x16{};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  for (int qt = 0; qt < kAQT; ++qt) {
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt) oacc[vt][qt] = f32x16{};
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
+  }
 
   // per tile: this tile's fragments are in (own share: vmcnt; everyone's: the
   // barrier, after which the other buffer is free too), then the next tile's
@@ -491,12 +501,12 @@ __global__ __launch_bounds__(kNThreads, 1) void attend_kernel(AttendArgs a) {
   if (n_tiles > 0) fetch(0, smem);
   const int n_plain = min(mask_from, n_tiles);   // tiles every row sees whole
   int nt = 0;
-  for (; nt < n_plain; ++nt) attend_tile<false>(next(nt), qf, vis, nt, a.scale_log2, m, l, oacc);
-  for (; nt < n_tiles; ++nt) attend_tile<true>(next(nt), qf, vis, nt, a.scale_log2, m, l, oacc);
+  for (; nt < n_plain; ++nt) attend_tile<false, kAQT>(next(nt), qf, vis, nt, a.scale_log2, m, l, oacc);
+  for (; nt < n_tiles; ++nt) attend_tile<true, kAQT>(next(nt), qf, vis, nt, a.scale_log2, m, l, oacc);
 
   // out[b, i, h, v] = O / l; a row that sees no position yields zeros
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kAQT; ++qt) {
     const float lt = pair_sum(l[qt]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qi[qt] >= Sq) continue;
@@ -534,8 +544,8 @@ hipError_t launch_naive(const uint16_t* q_nope, const uint16_t* q_pe, const uint
   const AttendArgs aa{q_nope, q_pe, (const char*)ws, seq_lens, out, q_tokens, t64, max_len,
                       scale * 1.4426950408889634f};
   static_assert(kHeads % 8 == 0, "whole heads per XCD");
-  hipLaunchKernelGGL(attend_kernel, dim3((q_tokens + kQPerWg - 1) / kQPerWg * kHeads, 1, batch), dim3(kNThreads), 0,
-                     stream, aa);
+  hipLaunchKernelGGL(attend_kernel, dim3((q_tokens + kQPerWg - 1) / kQPerWg * kHeads, 1, batch),
+                     dim3(kAWaves * 64), 0, stream, aa);
   return hipGetLastError();
 }
 
