@@ -51,6 +51,7 @@ def test_prefill_every_head(spec):
     synth.Spec("chunked_prefill", 2, 100, (200, 129)),
     synth.Spec("rows_see_nothing", 2, 70, (50, 300)),
     synth.Spec("decode_sq2_ragged", 3, 2, (2, 129, 1000)),
+    synth.Spec("empty_and_single", 3, 2, (0, 1, 65), max_seq_len=128),
 ], ids=lambda s: s.name)
 def test_partial_prefill_and_short_sequences(spec):
     batch = synth.make_batch(spec, seed=7 + spec.q_tokens)
@@ -60,6 +61,9 @@ def test_partial_prefill_and_short_sequences(spec):
     if spec.name == "rows_see_nothing":
         # sequence 0 (L = 50 < Sq = 70): rows 0..19 see no position -> zeros
         assert np.all(got[0, :20] == 0.0)
+    if spec.name == "empty_and_single":
+        # L = 0: no row sees anything; L = 1: row 0 sees nothing
+        assert np.all(got[0] == 0.0) and np.all(got[1, 0] == 0.0)
     assert_parity(got, ref, spec.name)
 
 

@@ -147,3 +147,14 @@ def test_shared_workspace_after_a_larger_plan():
     torch.cuda.synchronize()
     assert np.isfinite(want).all()
     assert np.array_equal(got, want)
+
+
+def test_rows_that_see_nothing_are_zero():
+    """L = 0 (both rows see nothing) and L = 1 < Sq = 2 (row 0 sees nothing,
+    row 1 sees position 0): those rows are zeros; the rest match the oracle."""
+    spec = synth.Spec("short_seqs", 4, 2, (1, 0, 2, 70), max_seq_len=128)
+    batch = synth.make_batch(spec, seed=29)
+    say(f"case {spec.name}: lens={batch['seq_lens'].tolist()}")
+    got = run_gpu(batch)
+    assert np.all(got[1] == 0.0) and np.all(got[0, 0] == 0.0)
+    assert_parity(got, oracle(batch), spec.name)
