@@ -302,6 +302,60 @@ def time_query_project(lib, dec, d, B, Sq, stream, args) -> dict:
     return out
 
 
+def time_prologue(lib, dec, d, B, Sq, stream, args) -> dict:
+    """The decode-step prologue (mla_project_new_tokens: the cache append and
+    the query side of the new tokens in one call, W_DQ and [W_DKV; W_KR]
+    streamed together), HIP events around the calls; weight copies rotate
+    past the Infinity Cache."""
+    import torch
+    from mla_latent_kv_amd import binding, synth
+    rows = B * Sq
+    qin = synth.make_query_inputs(B, Sq, seed=3000)
+    ain = synth.make_append_inputs(B, Sq, seed=1000)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    hid = bf16(qin["hidden"])
+    w0 = (dec.pack(bf16(qin["w_dq"])), dec.pack(bf16(qin["w_uq"])),
+          dec.pack(bf16(np.concatenate([ain["w_dkv"], ain["w_kr"]]))))
+    wbytes = QPROJ_WEIGHT_BYTES + APPEND_WEIGHT_BYTES
+    n_w = max(2, math.ceil(MALL_BYTES / wbytes) + 1)
+    ws = [w0] + [tuple(w.clone() for w in w0) for _ in range(n_w - 1)]
+    cache = d["kv_cache"].clone()
+    qn = torch.empty((B, Sq, 128, 128), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((B, Sq, 128, 64), dtype=torch.bfloat16, device="cuda")
+    need = binding.mla_project_new_tokens_workspace_size(dec.ctx, B, Sq)
+    wsp = torch.empty(need, dtype=torch.uint8, device="cuda")
+    cargs = [binding.MlaPrologueArgs(hid.data_ptr(), a.data_ptr(), b.data_ptr(), c.data_ptr(), cache.data_ptr(),
+                                     d["block_table"].data_ptr(), d["seq_lens"].data_ptr(), qn.data_ptr(),
+                                     qp.data_ptr(), cache.shape[0], B, Sq, d["block_table"].shape[1], 0.0)
+             for a, b, c in ws]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(i):
+        rc = lib.mla_project_new_tokens(dec.ctx, ctypes.byref(cargs[i % n_w]), ctypes.c_void_p(wsp.data_ptr()),
+                                        need, sh)
+        if rc != 0:
+            raise RuntimeError(binding.mla_decode_status_string(rc))
+
+    for i in range(max(2, args.warmup // 2)):
+        call(i)
+    torch.cuda.synchronize()
+    n = max(4, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    nbytes = wbytes + rows * 7168 * 2 + rows * 128 * 192 * 2 + rows * 1152
+    return {"us_per_call": us, "tokens": rows, "rotating_weight_sets": n_w, "calls": n,
+            "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "launches": 3}
+
+
 PREFILL_SPEC = ("prefill_b1_l4096", 1, 4096)   # one 4096-token prompt, every token a query
 
 
@@ -517,6 +571,9 @@ def main() -> int:
     if not args.no_append:
         result["cache_append"] = time_cache_append(lib, dec, d, B, Sq, stream, args)
         result["query_project"] = time_query_project(lib, dec, d, B, Sq, stream, args)
+        result["prologue"] = time_prologue(lib, dec, d, B, Sq, stream, args)
+        result["prologue"]["separate_calls_us"] = (result["cache_append"]["us_per_call"]
+                                                   + result["query_project"]["us_per_call"])
         result["output_project"] = time_output_project(lib, dec, B, Sq, stream, args)
         result["naive"] = time_naive(lib, dec, d, B, Sq, stream, args, ms)
     if not args.no_cpu:

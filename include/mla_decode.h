@@ -251,6 +251,40 @@ int mla_query_project_workspace_size(const mla_decode_ctx* ctx, int32_t batch, i
 int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* args, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* ---- Decode-step prologue: cache append and query side together -----------
+ *
+ * mla_cache_append and mla_query_project for the same new tokens in one call:
+ * W_DQ and [W_DKV; W_KR] both read the hidden states h, so they are streamed
+ * side by side in one product and one split sum finishes both (c_Q for the
+ * second query product, the cache rows). Results: the cache rows of
+ * mla_cache_append and the q_nope / q_pe of mla_query_project, with the same
+ * bounds (the q values are bit-identical to mla_query_project's: the c_Q sums
+ * run in the same order). Three kernels on `stream` instead of five; the
+ * arguments and layouts are those of the two calls. Errors as for
+ * mla_decode_run. */
+typedef struct mla_prologue_args {
+  const void* hidden;          /* bf16 [B, Sq, 7168] */
+  const void* w_dq;            /* packed W_DQ, 1536 x 7168 */
+  const void* w_uq;            /* packed W_UQ, 24576 x 1536 */
+  const void* w_kv;            /* packed [W_DKV; W_KR], 576 x 7168 */
+  void* kv_cache;              /* bf16 [num_blocks, 64, 576]; the new tokens' rows written */
+  const int32_t* block_table;  /* int32 [B, max_blocks_per_seq] */
+  const int32_t* seq_lens;     /* int32 [B], counting the new tokens */
+  void* q_nope;                /* bf16 [B, Sq, 128, 128], written */
+  void* q_pe;                  /* bf16 [B, Sq, 128, 64], written */
+  int64_t num_blocks;          /* blocks in kv_cache */
+  int32_t batch;               /* 1 <= B <= 1000000 */
+  int32_t q_tokens;            /* Sq: 1 or 2, <= max_q_tokens */
+  int32_t max_blocks_per_seq;  /* row stride of block_table */
+  float rope_base;             /* <= 0 selects 10000 */
+} mla_prologue_args;
+
+int mla_project_new_tokens_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                                          size_t* bytes);
+
+int mla_project_new_tokens(const mla_decode_ctx* ctx, const mla_prologue_args* args, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* ---- Output projection -----------------------------------------------------
  *
  * y[t, :] = W_O x_t: the attention outputs of token t (the `out` of

@@ -80,6 +80,25 @@ class MlaQueryArgs(ctypes.Structure):
     ]
 
 
+class MlaPrologueArgs(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_void_p),
+        ("w_dq", ctypes.c_void_p),
+        ("w_uq", ctypes.c_void_p),
+        ("w_kv", ctypes.c_void_p),
+        ("kv_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("q_nope", ctypes.c_void_p),
+        ("q_pe", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("batch", ctypes.c_int32),
+        ("q_tokens", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+    ]
+
+
 class MlaOprojArgs(ctypes.Structure):
     _fields_ = [
         ("x", ctypes.c_void_p),
@@ -145,6 +164,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_query_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaQueryArgs),
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_query_project.restype = ctypes.c_int
+    lib.mla_project_new_tokens_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_project_new_tokens_workspace_size.restype = ctypes.c_int
+    lib.mla_project_new_tokens.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaPrologueArgs), ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_project_new_tokens.restype = ctypes.c_int
     lib.mla_output_project_workspace_size.argtypes = [ctypes.c_void_p, ctypes.c_int32,
                                                       ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_output_project_workspace_size.restype = ctypes.c_int
@@ -388,6 +413,56 @@ def mla_query_project(ctx, hidden, w_dq, w_uq, seq_lens, rope_base: float = 0.0,
     return q_nope, q_pe
 
 
+def mla_project_new_tokens_workspace_size(ctx, batch: int, q_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mla_project_new_tokens_workspace_size(ctx, int(batch), int(q_tokens),
+                                                                ctypes.byref(n)),
+           "mla_project_new_tokens_workspace_size")
+    return n.value
+
+
+def mla_project_new_tokens(ctx, hidden, w_dq, w_uq, w_kv, kv_cache, block_table, seq_lens,
+                           rope_base: float = 0.0, q_nope=None, q_pe=None, workspace=None, stream=None):
+    """Enqueue the decode-step prologue: the new tokens' cache rows (as
+    mla_cache_append) and their queries (as mla_query_project) in one call.
+    Weights packed by mla_pack_weight. Returns (q_nope, q_pe); kv_cache is
+    written in place."""
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _require(hidden, "hidden", b16, 3)
+    _require_packed(w_dq, "w_dq", 1536, D_HIDDEN)
+    _require_packed(w_uq, "w_uq", N_HEADS * (D_NOPE + D_ROPE), 1536)
+    _require_packed(w_kv, "w_kv", D_LATENT + D_ROPE, D_HIDDEN)
+    _require(kv_cache, "kv_cache", b16, 3)
+    _require(block_table, "block_table", (torch.int32,), 2)
+    _require(seq_lens, "seq_lens", (torch.int32,), 1)
+    B, Sq = hidden.shape[0], hidden.shape[1]
+    if hidden.shape[2] != D_HIDDEN:
+        raise ValueError("hidden must be [B, Sq, 7168]")
+    if tuple(kv_cache.shape[1:]) != (BLOCK, D_LATENT + D_ROPE):
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table / seq_lens batch mismatch")
+    if q_nope is None:
+        q_nope = torch.empty((B, Sq, N_HEADS, D_NOPE), dtype=torch.bfloat16, device=hidden.device)
+    if q_pe is None:
+        q_pe = torch.empty((B, Sq, N_HEADS, D_ROPE), dtype=torch.bfloat16, device=hidden.device)
+    _require(q_nope, "q_nope", b16, 4)
+    _require(q_pe, "q_pe", b16, 4)
+    if tuple(q_nope.shape) != (B, Sq, N_HEADS, D_NOPE) or tuple(q_pe.shape) != (B, Sq, N_HEADS, D_ROPE):
+        raise ValueError("q_nope / q_pe shapes must be [B, Sq, 128, 128] / [B, Sq, 128, 64]")
+    workspace = _workspace(workspace, mla_project_new_tokens_workspace_size(ctx, B, Sq), hidden.device)
+    s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
+    args = MlaPrologueArgs(hidden.data_ptr(), w_dq.data_ptr(), w_uq.data_ptr(), w_kv.data_ptr(),
+                           kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), q_nope.data_ptr(),
+                           q_pe.data_ptr(), kv_cache.shape[0], B, Sq, block_table.shape[1], float(rope_base))
+    _check(load_library().mla_project_new_tokens(ctx, ctypes.byref(args), workspace.data_ptr(),
+                                                 workspace.numel() * workspace.element_size(),
+                                                 ctypes.c_void_p(s.cuda_stream)),
+           "mla_project_new_tokens")
+    return q_nope, q_pe
+
+
 def mla_output_project_workspace_size(ctx, rows: int) -> int:
     n = ctypes.c_size_t()
     _check(load_library().mla_output_project_workspace_size(ctx, int(rows), ctypes.byref(n)),
@@ -495,6 +570,10 @@ class MLADecoder:
     def query_project(self, *args, **kw):
         """Forwards to mla_query_project (q_nope, q_pe of the new tokens)."""
         return mla_query_project(self.ctx, *args, **kw)
+
+    def project_new_tokens(self, *args, **kw):
+        """Forwards to mla_project_new_tokens (cache rows and queries of the new tokens)."""
+        return mla_project_new_tokens(self.ctx, *args, **kw)
 
     def output_project(self, *args, **kw):
         """Forwards to mla_output_project (y = W_O x)."""

@@ -242,6 +242,45 @@ int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* a, void* 
   return status;
 }
 
+int mla_project_new_tokens_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,
+                                          size_t* bytes) {
+  if (!ctx || !bytes || batch < 1 || batch > mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
+  if (q_tokens < 1 || q_tokens > ctx->cfg.max_q_tokens) return MLA_ERR_INVALID_ARG;
+  *bytes = mla::prologue_workspace_bytes(batch * q_tokens);
+  return MLA_OK;
+}
+
+int mla_project_new_tokens(const mla_decode_ctx* ctx, const mla_prologue_args* a, void* workspace,
+                           size_t workspace_bytes, void* stream_handle) {
+  if (!ctx || !a || !a->hidden || !a->w_dq || !a->w_uq || !a->w_kv || !a->kv_cache || !a->block_table ||
+      !a->seq_lens || !a->q_nope || !a->q_pe)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->batch > mla::kMaxBatch || a->q_tokens < 1 || a->q_tokens > ctx->cfg.max_q_tokens ||
+      a->num_blocks < 1 || a->max_blocks_per_seq < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!(a->rope_base == a->rope_base)) return MLA_ERR_INVALID_ARG;   // NaN
+  if (!aligned16(a->hidden) || !aligned16(a->w_dq) || !aligned16(a->w_uq) || !aligned16(a->w_kv) ||
+      !aligned16(a->kv_cache) || !aligned16(a->block_table) || !aligned16(a->seq_lens) || !aligned16(a->q_nope) ||
+      !aligned16(a->q_pe))
+    return MLA_ERR_MISALIGNED;
+  const size_t need = mla::prologue_workspace_bytes(a->batch * a->q_tokens);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  const double base = a->rope_base > 0.f ? (double)a->rope_base : 10000.0;
+  const int status =
+      mla::launch_prologue((const uint16_t*)a->hidden, (const uint16_t*)a->w_dq, (const uint16_t*)a->w_uq,
+                           (const uint16_t*)a->w_kv, (uint16_t*)a->kv_cache, a->block_table, a->seq_lens,
+                           a->num_blocks, a->max_blocks_per_seq, (uint16_t*)a->q_nope, (uint16_t*)a->q_pe,
+                           a->batch, a->q_tokens, base, workspace, stream) == hipSuccess
+          ? MLA_OK
+          : MLA_ERR_HIP;
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
+}
+
 int mla_output_project_workspace_size(const mla_decode_ctx* ctx, int32_t rows, size_t* bytes) {
   if (!ctx || !bytes || rows < 1 || rows > 2 * mla::kMaxBatch) return MLA_ERR_INVALID_ARG;
   *bytes = mla::oproj_workspace_bytes(rows);

@@ -120,13 +120,22 @@ hipError_t launch_pack_weight(const uint16_t* w, uint16_t* packed, int n, int k,
 size_t oproj_workspace_bytes(int rows);
 hipError_t launch_oproj(const float* x, const uint16_t* w_o, float* y, int rows, void* ws, hipStream_t stream);
 
-// query side (four launches): q_nope / q_pe of the new tokens from h
+// query side (three launches): q_nope / q_pe of the new tokens from h
 size_t qproj_workspace_bytes(int rows);
 hipError_t launch_qproj(const uint16_t* hidden, const uint16_t* w_dq, const uint16_t* w_uq,
                         const int32_t* seq_lens, uint16_t* q_nope, uint16_t* q_pe, int batch,
                         int q_tokens, double rope_base, void* ws, hipStream_t stream);
 
-// cache-append producer (three launches): the new tokens' cache rows from h
+// decode-step prologue (three launches): the cache append and the query side
+// of the same new tokens, W_DQ and [W_DKV; W_KR] streamed side by side
+size_t prologue_workspace_bytes(int rows);
+hipError_t launch_prologue(const uint16_t* hidden, const uint16_t* w_dq, const uint16_t* w_uq,
+                           const uint16_t* w_kv, uint16_t* cache, const int32_t* block_table,
+                           const int32_t* seq_lens, long long num_blocks, int max_blocks_per_seq,
+                           uint16_t* q_nope, uint16_t* q_pe, int batch, int q_tokens, double rope_base, void* ws,
+                           hipStream_t stream);
+
+// cache-append producer (two launches): the new tokens' cache rows from h
 // and the packed stacked weight [W_DKV; W_KR] ([576][7168])
 size_t append_workspace_bytes(int rows);
 hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_kv, uint16_t* cache,

@@ -18,59 +18,36 @@
 //  2. the splits added in split order; c_Q (fp32) is written straight into
 //     the packed input layout of the second product;
 //  3. stream W_UQ: 256 column blocks of 96, one split (each wavefront 24
-//     k-steps); c_Q enters as fp32 hi + lo. Its epilogue finishes the heads:
-//     non-positional columns rounded to bf16, position pairs rotated (fp64
-//     angles) and rounded (nearest, ties to even).
+//     k-steps); c_Q enters as fp32 hi + lo. Its epilogue (rows.h) finishes
+//     the heads.
+// The decode-step prologue (mla_project_new_tokens) runs the cache append on
+// the same stream: W_DQ and [W_DKV; W_KR] both read h, so launch 1 streams
+// both weights side by side (66 column tiles) and launch 2 routes the
+// columns past 1536 to the cache rows.
+#include "rows.h"
 #include "wstream.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kQRank = 1536;
-constexpr int kQRow = kDNope + kDRope;   // 192 rows of W_UQ per head
-constexpr int kQUp = kHeads * kQRow;     // 24576
+using rows::kQRank;
+using rows::kQUp;
 using QDownPlan = ws::Plan<false, kQRank, kDHidden, 1, 7, 16, true>;
+using ProloguePlan = ws::Plan<false, kQRank + kRow, kDHidden, 1, 7, 16, true>;   // [W_DQ | W_KV] columns
 using QUpPlan = ws::Plan<true, kQUp, kQRank, 3, 4, 1>;
-static_assert(kQRow % 4 == 0 && kDNope % 4 == 0, "4 columns never straddle a head or the nope/rope boundary");
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-__device__ __forceinline__ unsigned int bf16_rne(float x) {
-  unsigned int u = __builtin_bit_cast(unsigned int, x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// q[r][c .. c + 3] (c % 4 == 0) -> q_nope / q_pe of token r, head c / 192
-struct HeadsEpi {
-  const int32_t* seq_lens;
-  uint16_t* q_nope;
-  uint16_t* q_pe;
-  int q_tokens;
-  double rope_base;
+// columns [0, 1536) -> packed c_Q; [1536, 2112) -> the token's cache row
+struct PrologueEpi {
+  ws::StorePackedF32 c_q;
+  rows::CacheRowEpi cache;
   __device__ void operator()(int r, int c, f32x4 v) const {
-    const int head = c / kQRow, j = c % kQRow;
-    const size_t rh = (size_t)r * kHeads + head;
-    if (j < kDNope) {
-      const u32x2 p = {bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
-      *(u32x2*)(q_nope + rh * kDNope + j) = p;
-      return;
-    }
-    const int b = r / q_tokens, i = r % q_tokens;
-    const double pos = (double)(seq_lens[b] - q_tokens + i);
-    const int jr = j - kDNope;   // first of two position pairs
-    unsigned int w[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int pair = jr / 2 + k;
-      const double theta = pow(rope_base, -2.0 * pair / kDRope);
-      double s, co;
-      sincos(pos * theta, &s, &co);
-      const double x0 = v[2 * k], x1 = v[2 * k + 1];
-      w[k] = bf16_rne((float)(x0 * co - x1 * s)) | (bf16_rne((float)(x0 * s + x1 * co)) << 16);
-    }
-    *(u32x2*)(q_pe + rh * kDRope + jr) = u32x2{w[0], w[1]};
+    if (c < kQRank)
+      c_q(r, c, v);
+    else
+      cache(r, c - kQRank, v);
   }
 };
 
@@ -91,7 +68,29 @@ hipError_t launch_qproj(const uint16_t* hidden, const uint16_t* w_dq, const uint
   // epilogue never stores
   const hipError_t e = QDownPlan::run(hidden, w_dq, part, rows, ws::StorePackedF32{cq, kQRank / 16}, stream);
   if (e != hipSuccess) return e;
-  return QUpPlan::run(cq, w_uq, nullptr, rows, HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rope_base}, stream);
+  return QUpPlan::run(cq, w_uq, nullptr, rows, rows::HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rope_base},
+                      stream);
+}
+
+size_t prologue_workspace_bytes(int rows) {
+  return round256(ProloguePlan::part_bytes(rows)) + round256(QUpPlan::packed_x_bytes(rows));
+}
+
+hipError_t launch_prologue(const uint16_t* hidden, const uint16_t* w_dq, const uint16_t* w_uq,
+                           const uint16_t* w_kv, uint16_t* cache, const int32_t* block_table,
+                           const int32_t* seq_lens, long long num_blocks, int max_blocks_per_seq,
+                           uint16_t* q_nope, uint16_t* q_pe, int batch, int q_tokens, double rope_base, void* ws,
+                           hipStream_t stream) {
+  const int rows = batch * q_tokens;
+  float* part = (float*)ws;
+  char* cq = (char*)ws + round256(ProloguePlan::part_bytes(rows));
+  const PrologueEpi epi{ws::StorePackedF32{cq, kQRank / 16},
+                        rows::CacheRowEpi{seq_lens, block_table, cache, num_blocks, max_blocks_per_seq, q_tokens,
+                                          rope_base}};
+  const hipError_t e = ProloguePlan::run2(hidden, w_dq, kQRank, w_kv, part, rows, epi, stream);
+  if (e != hipSuccess) return e;
+  return QUpPlan::run(cq, w_uq, nullptr, rows, rows::HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rope_base},
+                      stream);
 }
 
 }  // namespace mla

@@ -99,10 +99,16 @@ __global__ __launch_bounds__(256) void pack_x_kernel(const void* __restrict__ x,
 struct StreamArgs {
   const u32x4* xp;    // packed input
   const u32x4* wp;    // packed weight
-  int n_tiles;        // N / 32
+  int n_tiles;        // its column tiles (its N / 32)
   int k_steps;        // K / 16
   int rows;           // tokens
   int ks_per_wave;    // k-steps per wavefront (a multiple of kDepth, >= kDepth)
+  // optional second weight with the same K, packed on its own: column blocks
+  // cb >= cb2 stream wp2 (column block cb - cb2 of it); their outputs follow
+  // the first weight's columns
+  const u32x4* wp2;
+  int n_tiles2;
+  int cb2;
 };
 
 template <bool kXF32, int kCT>
@@ -128,8 +134,9 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(StreamArgs a, Epi e
   const int ks0 = (blockIdx.y * 4 + wv) * a.ks_per_wave;
   const int n = lane & 31, h = lane >> 5;
   constexpr int kXPer = kXF32 ? 128 : 64;   // 16-byte pieces per input k-step
-  const u32x4* wbase = a.wp + (size_t)cb * kCT * 64 + lane;
-  const size_t wstep = (size_t)a.n_tiles * 64;
+  const bool second = cb >= a.cb2;
+  const u32x4* wbase = (second ? a.wp2 + (size_t)(cb - a.cb2) * kCT * 64 : a.wp + (size_t)cb * kCT * 64) + lane;
+  const size_t wstep = (size_t)(second ? a.n_tiles2 : a.n_tiles) * 64;
   const u32x4* xbase =
       kXRows ? (const u32x4*)((const uint16_t*)a.xp +
                               (size_t)(32 * rt + n < a.rows ? 32 * rt + n : 0) * (16 * (size_t)a.k_steps) +
@@ -262,7 +269,16 @@ struct Plan {
   // (part_bytes(rows)) and the split-order sum.
   template <class Epi>
   static hipError_t run(const void* xp, const void* wp, float* part, int rows, Epi epi, hipStream_t stream) {
-    const StreamArgs a{(const u32x4*)xp, (const u32x4*)wp, kNTiles, kKSteps, rows, kKsPerWave};
+    return run2(xp, wp, kN, nullptr, part, rows, epi, stream);
+  }
+  // The same with two weights of this K side by side: wp's n1 columns, then
+  // wp2's kN - n1 (n1 a multiple of 32 kCT).
+  template <class Epi>
+  static hipError_t run2(const void* xp, const void* wp, int n1, const void* wp2, float* part, int rows, Epi epi,
+                         hipStream_t stream) {
+    const StreamArgs a{(const u32x4*)xp, (const u32x4*)wp, n1 / 32,          kKSteps,
+                       rows,             kKsPerWave,       (const u32x4*)wp2, (kN - n1) / 32,
+                       n1 / (32 * kCT)};
     const dim3 grid(kNTiles / kCT, kSplits, (rows + 31) / 32);
     if constexpr (kSplits == 1) {
       hipLaunchKernelGGL((stream_kernel<kXF32, kCT, kDepth, kXRows, Epi>), grid, dim3(kThreads), 0, stream, a,

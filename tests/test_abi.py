@@ -28,7 +28,8 @@ def test_every_declared_symbol_is_exported():
                         "mla_cache_append_workspace_size", "mla_output_project",
                         "mla_output_project_workspace_size", "mla_query_project",
                         "mla_query_project_workspace_size", "mla_pack_weight",
-                        "mla_naive_workspace_size", "mla_naive_run"}
+                        "mla_naive_workspace_size", "mla_naive_run",
+                        "mla_project_new_tokens_workspace_size", "mla_project_new_tokens"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -129,3 +130,14 @@ def test_naive_rejects_nulls_before_any_device_call():
     args = binding.MlaNaiveArgs()
     assert lib.mla_naive_run(None, ctypes.byref(args), None, 0, None) == -1
     assert lib.mla_naive_run(None, None, None, 0, None) == -1
+
+
+def test_prologue_rejects_nulls_before_any_device_call():
+    import ctypes
+    from mla_latent_kv_amd import binding
+    lib = _lib()
+    n = ctypes.c_size_t()
+    assert lib.mla_project_new_tokens_workspace_size(None, 4, 1, ctypes.byref(n)) == -1
+    args = binding.MlaPrologueArgs()
+    assert lib.mla_project_new_tokens(None, ctypes.byref(args), None, 0, None) == -1
+    assert lib.mla_project_new_tokens(None, None, None, 0, None) == -1
