@@ -34,7 +34,7 @@ hipError_t launch_append(const uint16_t* hidden, const uint16_t* w_kv, uint16_t*
   const int rows = batch * q_tokens;
   return AppendPlan::run(hidden, w_kv, (float*)ws, rows,
                          rows::CacheRowEpi{seq_lens, block_table, cache, num_blocks, max_blocks_per_seq, q_tokens,
-                                           rope_base},
+                                           rows::RopeFreq::make(rope_base)},
                          stream);
 }
 

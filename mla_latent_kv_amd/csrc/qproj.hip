@@ -68,7 +68,7 @@ hipError_t launch_qproj(const uint16_t* hidden, const uint16_t* w_dq, const uint
   // epilogue never stores
   const hipError_t e = QDownPlan::run(hidden, w_dq, part, rows, ws::StorePackedF32{cq, kQRank / 16}, stream);
   if (e != hipSuccess) return e;
-  return QUpPlan::run(cq, w_uq, nullptr, rows, rows::HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rope_base},
+  return QUpPlan::run(cq, w_uq, nullptr, rows, rows::HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rows::RopeFreq::make(rope_base)},
                       stream);
 }
 
@@ -86,10 +86,10 @@ hipError_t launch_prologue(const uint16_t* hidden, const uint16_t* w_dq, const u
   char* cq = (char*)ws + round256(ProloguePlan::part_bytes(rows));
   const PrologueEpi epi{ws::StorePackedF32{cq, kQRank / 16},
                         rows::CacheRowEpi{seq_lens, block_table, cache, num_blocks, max_blocks_per_seq, q_tokens,
-                                          rope_base}};
+                                          rows::RopeFreq::make(rope_base)}};
   const hipError_t e = ProloguePlan::run2(hidden, w_dq, kQRank, w_kv, part, rows, epi, stream);
   if (e != hipSuccess) return e;
-  return QUpPlan::run(cq, w_uq, nullptr, rows, rows::HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rope_base},
+  return QUpPlan::run(cq, w_uq, nullptr, rows, rows::HeadsEpi{seq_lens, q_nope, q_pe, q_tokens, rows::RopeFreq::make(rope_base)},
                       stream);
 }
 

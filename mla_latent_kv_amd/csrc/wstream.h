@@ -280,6 +280,8 @@ struct Plan {
                        rows,             kKsPerWave,       (const u32x4*)wp2, (kN - n1) / 32,
                        n1 / (32 * kCT)};
     const dim3 grid(kNTiles / kCT, kSplits, (rows + 31) / 32);
+    if (kSplits > 1 && part == nullptr) return hipErrorInvalidValue;   // split sums need their buffer
+    if (n1 % (32 * kCT) != 0 || n1 > kN || (n1 < kN && wp2 == nullptr)) return hipErrorInvalidValue;
     if constexpr (kSplits == 1) {
       hipLaunchKernelGGL((stream_kernel<kXF32, kCT, kDepth, kXRows, Epi>), grid, dim3(kThreads), 0, stream, a,
                          epi);
