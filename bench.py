@@ -45,9 +45,9 @@ QPROJ_WEIGHT_BYTES = (1536 * 7168 + 128 * 192 * 1536) * 2   # W_DQ and W_UQ, bf1
 # the same counter reads for a plain device copy of known size (--copy-probe).
 # The figures belong to the attention source they were taken on: when the
 # source hash differs, traffic is reported as null.
-ATTN_TRAFFIC = {"src_sha256": "c952efa6f52f6c011759083ed552a4483b7bc3ba06ea616f79b8ddc0d328f38a",
-                "fetch_kib": 76215.167, "write_kib": 32896.0,
-                "fetch_scale": 1.99995, "write_scale": 1.0}
+ATTN_TRAFFIC = {"src_sha256": "7473bccc42bfc0cf8bb82bcd2ea7daf373abc837c608e5a9436a05de5d991085",
+                "fetch_kib": 76215.202, "write_kib": 32896.0,
+                "fetch_scale": 1.99994, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
 
 
@@ -110,6 +110,27 @@ def _elapsed(hip, a, b):
     return ms.value
 
 
+def copy_bandwidth(mib: int = 1024, reps: int = 5) -> dict:
+    """A plain device-to-device copy of `mib` MiB on the same GPU (torch's
+    copy kernel), timed with events: the practical HBM ceiling beside the
+    published 8 TB/s."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return {"bytes_read_and_written": 2 * n, "TBps": 2 * n / s / 1e12}
+
+
 def cpu_baseline(batch, budget_s: float, max_seqs: int) -> dict:
     """The fp64 oracle (naive path) on whole sequences of the batch until the
     time budget is spent; reported as query tokens per second."""
@@ -131,9 +152,18 @@ def cpu_baseline(batch, budget_s: float, max_seqs: int) -> dict:
             break
     dt = time.perf_counter() - t0
     q = done * batch["q_nope"].shape[1]
+    # the absorb-order routine of the oracle (the GPU path's algorithm, fp64)
+    # on the whole batch
+    ta = time.perf_counter()
+    orc.decode_batch(batch["q_nope"], batch["q_pe"], batch["w_uk"], batch["w_uv"], batch["cache"],
+                     batch["block_table"], batch["seq_lens"], batch["block_size"], path="absorb")
+    da = time.perf_counter() - ta
+    qa = B * batch["q_nope"].shape[1]
     return {"value": q / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {B} sequences ({done * int(batch['seq_lens'][0])} cached "
-                      f"tokens x 128 heads), fp64 NumPy naive path, {dt:.1f} s"}
+                      f"tokens x 128 heads), fp64 NumPy naive path, {dt:.1f} s",
+            "absorb_order": {"value": qa / da, "unit": "query-tokens/s",
+                             "sample": f"all {B} sequences, fp64 NumPy absorb order, {da:.2f} s"}}
 
 
 def time_cache_append(lib, dec, d, B, Sq, stream, args) -> dict:
@@ -523,9 +553,12 @@ def main() -> int:
     # stage boundaries: 1 -> 2 plan + absorb (prep), 2 -> 3 attention, 3 -> 4 merge + W_UV
     names = {1: "prep", 2: "attention", 3: "merge"}
     kern_ms = {n: 0.0 for n in names.values()}
+    step_ms = []
     for i in range(n_prof):
         for j, n in names.items():
             kern_ms[n] += _elapsed(hip, evs[5 * i + j], evs[5 * i + j + 1]) / n_prof
+        step_ms.append(_elapsed(hip, evs[5 * i], evs[5 * i + 4]))
+    step_pct = {f"p{q}": float(np.percentile(step_ms, q)) for q in (10, 50, 90)}
     for e in evs:
         hip.hipEventDestroy(e)
 
@@ -553,6 +586,8 @@ def main() -> int:
         "total_TBps": work["total_bytes"] / step_s / 1e12,
         "mfma_TFLOPs": work["flops"] / step_s / 1e12,
         "warm_ms_per_step": warm_ms,
+        "step_ms_percentiles": dict(step_pct, steps=n_prof,
+                                    note="first to last launch of one step, events between launches"),
         "kernel_ms": kern_ms,
         "roofline": {
             "bound": "hbm",
@@ -576,6 +611,7 @@ def main() -> int:
                                                    + result["query_project"]["us_per_call"])
         result["output_project"] = time_output_project(lib, dec, B, Sq, stream, args)
         result["naive"] = time_naive(lib, dec, d, B, Sq, stream, args, ms)
+    result["copy_bandwidth"] = copy_bandwidth()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0])
     print(json.dumps(result), flush=True)
