@@ -258,10 +258,10 @@ int mla_query_project(const mla_decode_ctx* ctx, const mla_query_args* args, voi
  * side by side in one product and one split sum finishes both (c_Q for the
  * second query product, the cache rows). Results: the cache rows of
  * mla_cache_append and the q_nope / q_pe of mla_query_project, with the same
- * bounds (the q values are bit-identical to mla_query_project's: the c_Q sums
- * run in the same order). Three kernels on `stream` instead of five; the
- * arguments and layouts are those of the two calls. Errors as for
- * mla_decode_run. */
+ * bounds (the compressed query's fp32 sums are split differently, so a q
+ * value can differ from mla_query_project's in its last bit). Three kernels
+ * on `stream` instead of five; the arguments and layouts are those of the two
+ * calls. Errors as for mla_decode_run. */
 typedef struct mla_prologue_args {
   const void* hidden;          /* bf16 [B, Sq, 7168] */
   const void* w_dq;            /* packed W_DQ, 1536 x 7168 */

@@ -12,9 +12,10 @@
 //
 // Three launches on the caller's stream (weight-stream products, wstream.h),
 // all deterministic:
-//  1. stream W_DQ: 48 column tiles x 16 K-splits = 768 workgroups, each
-//     wavefront with all its 7 k-steps in flight at once (h read from its
-//     rows), partial sums per split;
+//  1. stream W_DQ: 16 column blocks of 96 x 16 K-splits = 256 workgroups,
+//     each wavefront with all its 7 k-steps (3 column tiles each) in flight
+//     at once (h read from its rows, once per 3 column tiles), partial sums
+//     per split;
 //  2. the splits added in split order; c_Q (fp32) is written straight into
 //     the packed input layout of the second product;
 //  3. stream W_UQ: 256 column blocks of 96, one split (each wavefront 24
@@ -22,8 +23,12 @@
 //     the heads.
 // The decode-step prologue (mla_project_new_tokens) runs the cache append on
 // the same stream: W_DQ and [W_DKV; W_KR] both read h, so launch 1 streams
-// both weights side by side (66 column tiles) and launch 2 routes the
-// columns past 1536 to the cache rows.
+// both weights side by side (22 column blocks of 96 x 8 K-splits = 176
+// workgroups, each wavefront with all its 14 k-steps in flight) and launch 2
+// routes the columns past 1536 to the cache rows. The tilings of launch 1
+// were chosen by measurement (a sweep of column tiles, splits and ring
+// depths at 32 tokens); with 8 splits here and 16 in the query side alone,
+// the two calls' c_Q sums differ in order, i.e. in the last bit.
 #include "rows.h"
 #include "wstream.h"
 
@@ -33,8 +38,8 @@ namespace {
 
 using rows::kQRank;
 using rows::kQUp;
-using QDownPlan = ws::Plan<false, kQRank, kDHidden, 1, 7, 16, true>;
-using ProloguePlan = ws::Plan<false, kQRank + kRow, kDHidden, 1, 7, 16, true>;   // [W_DQ | W_KV] columns
+using QDownPlan = ws::Plan<false, kQRank, kDHidden, 3, 7, 16, true>;
+using ProloguePlan = ws::Plan<false, kQRank + kRow, kDHidden, 3, 14, 8, true>;   // [W_DQ | W_KV] columns
 using QUpPlan = ws::Plan<true, kQUp, kQRank, 3, 4, 1>;
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
