@@ -83,8 +83,11 @@ typedef struct mla_decode_config {
   int32_t block_size;    /* 64 */
   int32_t max_q_tokens;  /* 1 or 2 */
   float softmax_scale;   /* <= 0 selects 1/sqrt(d_nope + d_rope) */
-  int32_t split_target;  /* about how many splits to cut a batch into; 0 = one
-                            per compute unit (Sq = 1) or per two (Sq = 2) */
+  int32_t split_target;  /* attention work slots that run at once (each is one
+                            workgroup for Sq = 1, two for Sq = 2); the plan
+                            cuts the batch into at most 4 rounds of them.
+                            0 = one per compute unit (Sq = 1) or per two
+                            (Sq = 2) */
 } mla_decode_config;
 
 typedef struct mla_decode_args {

@@ -126,7 +126,8 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
   };
   int status = MLA_OK;
   if (!mark(0) || !mark(1) ||
-      mla::launch_prep(a->seq_lens, a->batch, max_len, target, L.max_chunks, work, seqinfo, meta,
+      mla::launch_prep(a->seq_lens, a->batch, max_len, target, L.positions, L.depth, L.max_chunks, work,
+                       seqinfo, meta,
                        (const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,
                        stream) != hipSuccess) {
     status = MLA_ERR_HIP;
@@ -145,10 +146,12 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
     aa.max_blocks_per_seq = a->max_blocks_per_seq;
     aa.q_tokens = a->q_tokens;
     aa.max_chunks = L.max_chunks;
+    aa.positions = L.positions;
+    aa.depth = L.depth;
     aa.scale_log2 = ctx->scale * 1.4426950408889634f;
     if (!mark(2) || mla::launch_attn(aa, stream) != hipSuccess || !mark(3) ||
         mla::launch_merge(part_o, part_lse, seqinfo, (const uint16_t*)a->w_uv, a->out, a->batch,
-                          a->q_tokens, stream) != hipSuccess ||
+                          a->q_tokens, L.max_chunks, stream) != hipSuccess ||
         !mark(4))
       status = MLA_ERR_HIP;
   }

@@ -145,12 +145,13 @@ __device__ __forceinline__ f16x8 lds_read_tr(const char* p0, const char* p1) {
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
-  // ---- which split / which half of the heads. Workgroups are dealt to the 8
-  // XCDs round-robin by id (XCD = id % 8); the plan stores the work list so
-  // that position p holds an item of XCD p % 8 and each XCD runs a contiguous
-  // run of items (consecutive splits of the same sequences share one L2 and
-  // their queries are fetched into it once). With Sq = 2 the two head halves
-  // of a split are ids 8 apart: same XCD, dispatched together.
+  // ---- which position / which half of the heads. Workgroups are dealt to
+  // the 8 XCDs round-robin by id (XCD = id % 8); the plan stores the work list
+  // so that position p holds items of XCD p % 8 and each XCD runs a
+  // contiguous run of slots (consecutive splits of the same sequences share
+  // one L2 and their queries are fetched into it once). With Sq = 2 the two
+  // head halves of a position are ids 8 apart: same XCD, dispatched together.
+  // A workgroup runs the entries of its position one after another.
   int pos, grp;
   if (p.q_tokens == 1) {
     pos = blockIdx.x;
@@ -159,13 +160,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     pos = ((blockIdx.x >> 4) << 3) + (blockIdx.x & 7);
     grp = (blockIdx.x >> 3) & 1;
   }
-  if (pos >= (p.max_chunks + 7) / 8 * 8) return;
-  const WorkItem wi = p.work[pos];
-  if (wi.slot < 0 || wi.slot >= p.max_chunks || wi.t_end <= wi.t_begin) return;
+  if (pos >= p.positions) return;
+  for (int item = 0; item < p.depth; ++item) {
+  const WorkItem wi = p.work[(size_t)item * p.positions + pos];
+  if (wi.slot < 0 || wi.slot >= p.max_chunks || wi.t_end <= wi.t_begin) break;
   const int b = wi.b;
   const int L = wi.len;
 
-  const int t = threadIdx.x;
+  // the thread index is made opaque per item, so that nothing derived from it
+  // is hoisted out of the item loop (its registers would stay live across the
+  // whole body, which already fills the register file)
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (SGPR)
   const int half = lane >> 5;
@@ -604,14 +610,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     const size_t prow = (size_t)row_qi(g) * kHeads + row_hg(g) * 32 + j;
     *(u32x4*)(dst + prow * kDLat + 8 * c16) = v;
   }
+  // the next item's fetches refill the buffers this epilogue read
+  MLA_WAIT_LGKM0();
+  MLA_BARRIER();
+  }   // item
 }
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   // one workgroup per work-list position (two for Sq = 2)
-  const int per = (a.max_chunks + 7) / 8 * 8;
-  const int grid = a.q_tokens == 1 ? per : 2 * per;
+  const int grid = a.q_tokens == 1 ? a.positions : 2 * a.positions;
   hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

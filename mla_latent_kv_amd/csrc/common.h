@@ -27,6 +27,8 @@ constexpr int kWaves = 4;               // wavefronts per workgroup
 constexpr int kRowsPerWg = kRowsPerWave * kWaves;   // 128
 constexpr int kMinChunk = 64;           // split granularity (one cache block)
 constexpr int kMaxBatch = 1000000;      // keeps the plan's packed 21-bit counters exact
+constexpr int kPlanWaves = 4;           // the plan fills the positions at most this many times over
+constexpr int kPlanSortMax = 1024;      // batches up to this size get the searched, sorted plan
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -40,7 +42,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // One split of one sequence: tokens [t_begin, t_end) of sequence b (whose
 // effective length is len); its partial softmax state goes to slot `slot`.
-// slot < 0 marks an unused entry of the work list.
+// slot < 0 marks an unused entry of the work list. The list is [depth][positions]:
+// the attention workgroup(s) of position p run entries (0, p), (1, p), ... up to
+// the first unused one.
 struct WorkItem {
   int b, t_begin, t_end, slot, len, pad0, pad1, pad2;
 };
@@ -54,14 +58,16 @@ struct SeqInfo {
 // Byte offsets of each region inside the caller's workspace.
 struct Layout {
   size_t work, seqinfo, meta, qabs, part_o, part_lse, total;
-  int max_chunks;   // capacity of the work list / partial slots
+  int max_chunks;   // capacity of the partial slots
+  int positions;    // work-list positions: the split target rounded up to 8
+  int depth;        // work-list entries per position
   int rows;         // B * Sq query rows
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split target: the plan aims for about this many chunks (workgroups for
-// Sq = 1; each chunk is two workgroups for Sq = 2).
+// Split target P: the number of work slots the plan fills at once (one
+// workgroup each for Sq = 1, two for Sq = 2), i.e. one per CU.
 inline int default_split_target(int n_cu, int q_tokens) {
   return q_tokens == 1 ? n_cu : n_cu / 2;
 }
@@ -69,15 +75,19 @@ inline int default_split_target(int n_cu, int q_tokens) {
 inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_target) {
   Layout L{};
   const int max_blocks = (max_seq_len + kBlock - 1) / kBlock;
-  long long cap = (long long)split_target + batch;   // sum_b ceil(L_b / C) <= total/C + B
-  long long by_len = (long long)batch * max_blocks;  // chunks are >= one block
+  // items: at most kPlanWaves * P on the searched plan, P + B on the simple
+  // one (sum_b ceil(L_b / C) <= total / C + B with C >= total / P); either way
+  // no more than one per cache block
+  L.positions = (split_target + 7) / 8 * 8;
+  L.depth = kPlanWaves + (batch + split_target - 1) / split_target;
+  long long cap = (long long)L.depth * split_target;
+  long long by_len = (long long)batch * max_blocks;
   L.max_chunks = (int)(cap < by_len ? cap : by_len);
   if (L.max_chunks < 1) L.max_chunks = 1;
   L.rows = batch * q_tokens;
   const size_t rows_per_chunk = (size_t)q_tokens * kHeads;
   size_t off = 0;
-  // the work list is stored XCD-interleaved and padded to a multiple of 8
-  L.work = off;    off = align_up(off + sizeof(WorkItem) * ((L.max_chunks + 7) / 8 * 8), 256);
+  L.work = off;    off = align_up(off + sizeof(WorkItem) * (size_t)L.depth * L.positions, 256);
   L.seqinfo = off; off = align_up(off + sizeof(SeqInfo) * batch, 256);
   L.meta = off;    off = align_up(off + 64, 256);
   L.qabs = off;    off = align_up(off + (size_t)L.rows * kHeads * kDLat * 2, 256);
@@ -90,7 +100,7 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
 // ---- launchers (each returns hipGetLastError() of its launch)
 // split plan + absorb product (one launch)
 hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target,
-                       int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
+                       int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
                        hipStream_t stream);
 struct AttnArgs {
@@ -107,6 +117,8 @@ struct AttnArgs {
   int max_blocks_per_seq;
   int q_tokens;
   int max_chunks;
+  int positions;      // work-list positions (one workgroup each; two for Sq = 2)
+  int depth;          // work-list entries per position
   float scale_log2;   // softmax scale * log2(e)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
@@ -151,7 +163,7 @@ hipError_t launch_naive(const uint16_t* q_nope, const uint16_t* q_pe, const uint
                         float scale, void* ws, hipStream_t stream);
 
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const SeqInfo* seqinfo,
-                        const uint16_t* w_uv, float* out, int batch, int q_tokens,
+                        const uint16_t* w_uv, float* out, int batch, int q_tokens, int max_chunks,
                         hipStream_t stream);
 
 }  // namespace mla

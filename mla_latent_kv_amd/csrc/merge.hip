@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
                                                           const SeqInfo* __restrict__ seqinfo,
                                                           const uint16_t* __restrict__ w_uv,
                                                           float* __restrict__ out, int rows,
-                                                          int q_tokens, int groups) {
+                                                          int q_tokens, int groups, int max_chunks) {
   // o_lat of the workgroup's rows as bf16 hi / lo: [row][64 granules of 8],
   // granule g of row r stored at g ^ r (16 rows: 16 different bank groups)
   __shared__ __attribute__((aligned(16))) unsigned short lat[2][kMRows * kDLat];
@@ -82,7 +82,10 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
   if (r < rows) {
     const SeqInfo si = seqinfo[r / q_tokens];
     const size_t prow = (size_t)(r % q_tokens) * kHeads + h;
-    const int base = si.base, cnt = si.count;
+    // the slot range stays inside the partial states (memory safety only: the
+    // plan never writes a range past them)
+    const int base = min(max(si.base, 0), max_chunks);
+    const int cnt = min(max(si.count, 0), max_chunks - base);
     // chunks of kChunk splits: the lse values and the partial rows of a chunk
     // are loaded in one round trip; a running max M rescales what earlier
     // chunks added (the same regrouping as the online softmax)
@@ -169,12 +172,12 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
 }  // namespace
 
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const SeqInfo* seqinfo,
-                        const uint16_t* w_uv, float* out, int batch, int q_tokens,
+                        const uint16_t* w_uv, float* out, int batch, int q_tokens, int max_chunks,
                         hipStream_t stream) {
   const int rows = batch * q_tokens;
   const int groups = (rows + kMRows - 1) / kMRows;
   hipLaunchKernelGGL(merge_kernel, dim3(kHeads * groups), dim3(kMThreads), 0, stream, part_o,
-                     part_lse, seqinfo, w_uv, out, rows, q_tokens, groups);
+                     part_lse, seqinfo, w_uv, out, rows, q_tokens, groups, max_chunks);
   return hipGetLastError();
 }
 

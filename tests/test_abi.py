@@ -66,22 +66,45 @@ def test_init_rejects_bad_q_tokens_and_nulls():
     lib.mla_decode_destroy(None)
 
 
-def test_workspace_layout_bounds():
-    """The split plan can never need more partial slots than the layout holds:
-    sum_b ceil(L_b / C) <= target + B when C >= total / target (host mirror of
-    the plan's arithmetic, checked on random lengths)."""
+def test_split_plan_invariants():
+    """The split plan (host mirror of the prep kernel's plan) on random
+    batches, both its searched and its simple form: every sequence's tokens
+    covered once by 64-aligned pieces, partial slots contiguous per sequence
+    and within the workspace's capacity, each position's entries dense."""
     import numpy as np
+    from tests import plan_mirror as pm
     rng = np.random.default_rng(0)
-    for _ in range(2000):
-        B = int(rng.integers(1, 300))
-        target = int(rng.integers(1, 600))
-        max_len = int(rng.integers(1, 200000))
-        lens = rng.integers(0, max_len + 1, size=B)
-        total = int(lens.sum())
-        C = max(64, -(-max(1, -(-total // target)) // 64) * 64)
-        chunks = int(sum(-(-int(l) // C) for l in lens))
-        cap = min(target + B, B * -(-max_len // 64))
-        assert chunks <= cap
+    for _ in range(1500):
+        B = int(rng.choice([1, 2, 3, 7, 32, 64, 128, 255, 256, 300, 1024, 1025, 2000]))
+        P = int(rng.choice([1, 7, 8, 128, 256, 1000]))
+        mx = int(rng.choice([1, 63, 64, 65, 512, 4096, 40000, 131072]))
+        kind = rng.integers(0, 4)
+        if kind == 0:
+            lens = rng.integers(0, mx + 1, B)
+        elif kind == 1:
+            lens = np.full(B, mx)
+        elif kind == 2:
+            lens = np.where(rng.random(B) < 0.5, 0, rng.integers(1, mx + 1, B))
+        else:
+            lens = rng.integers(-5, mx + 50, B)
+        pm.check(lens, mx, P)
+
+
+def test_split_plan_choices_on_the_workloads():
+    """The searched plan picks one round for equal lengths and several for
+    ragged ones: uniform 32 x 4096 -> 256 pieces of 512; the ragged and
+    two-token workloads -> more pieces than slots, each no longer than C."""
+    from mla_latent_kv_amd import synth
+    from tests import plan_mirror as pm
+    uni = synth.make_batch(synth.CONFIGS[1], seed=1)["seq_lens"]
+    r = pm.check(uni, 4096, 256)
+    assert r["search"] and r["C"] == 512 and r["n_items"] == 256
+    rag = synth.make_batch(synth.CONFIGS[2], seed=2)["seq_lens"]
+    r = pm.check(rag, 32768, 256)
+    assert r["search"] and 256 < r["n_items"] <= 4 * 256
+    mtp = synth.make_batch(synth.CONFIGS[4], seed=4)["seq_lens"]
+    r = pm.check(mtp, 16384, 128)
+    assert r["search"] and 128 < r["n_items"] <= 4 * 128
 
 
 def test_cache_append_rejects_nulls_before_any_device_call():
