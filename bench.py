@@ -45,8 +45,8 @@ QPROJ_WEIGHT_BYTES = (1536 * 7168 + 128 * 192 * 1536) * 2   # W_DQ and W_UQ, bf1
 # the same counter reads for a plain device copy of known size (--copy-probe).
 # The figures belong to the attention source they were taken on: when the
 # source hash differs, traffic is reported as null.
-ATTN_TRAFFIC = {"src_sha256": "7473bccc42bfc0cf8bb82bcd2ea7daf373abc837c608e5a9436a05de5d991085",
-                "fetch_kib": 76215.202, "write_kib": 32896.0,
+ATTN_TRAFFIC = {"src_sha256": "1368b85e54993382948c22110133e4167e20f71ee9ea2df179f8751659d45340",
+                "fetch_kib": 76243.167, "write_kib": 32896.0,
                 "fetch_scale": 1.99994, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
 
