@@ -55,6 +55,10 @@ CASES = [
     ("with_empty", synth.Spec("plan_empty", 4, 1, (0, 64, 65, 0)), 6, 0),
     ("target_7", synth.Spec("plan_t7", 4, 1, (700, 64, 4096, 1)), 7, 7),
     ("simple_b1100", synth.Spec("plan_b1100", 1100, 1, ("uniform", 1, 200)), 8, 0),
+    # searched plans with the largest sorts: 1024 sequences only fit in four
+    # rounds (1024 keys), 700 sequences pad the sort to 1024
+    ("sorted_b1024", synth.Spec("plan_b1024", 1024, 1, ("uniform", 1, 300)), 9, 0),
+    ("sorted_b700", synth.Spec("plan_b700", 700, 1, ("uniform", 1, 2000)), 10, 0),
 ]
 
 
