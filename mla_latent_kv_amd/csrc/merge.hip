@@ -8,18 +8,22 @@
 // "DeepSeek-V3" page, ailearn.mscapital.top, MLA section; m.lsln.cn article,
 // section 2.2).
 //
-// One workgroup of 8 wavefronts per (head, 16 query rows). The row groups of
-// one head run on one XCD (ids 8 apart), so W_UV[h] crosses HBM once and is
-// then served by that XCD's L2.
-//  1. thread (row, 32-lane slot) sums 2 units of 8 latent values over the
-//     row's splits, 8 splits per round trip (their lse values and 16-byte
-//     partial loads together; 32 lanes read 512 contiguous bytes of a partial
-//     row), with a running max across rounds; o_lat goes to LDS as bf16 hi +
-//     lo (hi = bf16(x), lo = bf16(x - hi), together within 2^-16 of x).
+// One workgroup of 8 wavefronts per (head, kR query rows), kR = 16, or 32
+// when there are more than 32 rows (each workgroup loads all of W_UV[h], so
+// wider groups load it fewer times; up to 32 rows the narrow groups keep at
+// least one workgroup per CU, which measured faster). The row groups of one head run on one
+// XCD (ids 8 apart), so W_UV[h] crosses HBM once and is then served by that
+// XCD's L2.
+//  1. thread (row, slot) sums 64 / (512 / kR) units of 8 latent values over
+//     the row's splits, several splits per round trip (their lse values and
+//     16-byte partial loads together; the slots of a row read contiguous
+//     bytes of a partial row), with a running max across rounds; o_lat goes
+//     to LDS as bf16 hi + lo (hi = bf16(x), lo = bf16(x - hi), together
+//     within 2^-16 of x).
 //  2. out^T[v, r] = W_UV[h][v, :] . o_lat[r, :] on 16x16x32 bf16 MFMA (W_UV
-//     exact, hi and lo accumulated in fp32): wavefront w owns value tile w
-//     (16 values); its W_UV fragments are loaded at the start and arrive while
-//     phase 1 streams the partials.
+//     exact, hi and lo accumulated in fp32), 16 rows per MFMA: wavefront w owns
+//     value tile w (16 values); its W_UV fragments are loaded at the start and
+//     arrive while phase 1 streams the partials.
 // No atomics: every output is written once, so results are deterministic.
 #include "common.h"
 
@@ -28,7 +32,6 @@ namespace mla {
 namespace {
 
 constexpr int kMThreads = 512;
-constexpr int kMRows = 16;        // query rows per workgroup
 constexpr int kKSteps = kDLat / 32;   // 16 k-steps of 32 latent values
 
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float x) {
@@ -41,20 +44,25 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short h) {
   return __builtin_bit_cast(float, (unsigned int)h << 16);
 }
 
+template <int kR>
 __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const SeqInfo* __restrict__ seqinfo,
                                                           const uint16_t* __restrict__ w_uv,
                                                           float* __restrict__ out, int rows,
                                                           int q_tokens, int groups, int max_chunks) {
+  static_assert(kR == 16 || kR == 32, "16 or 32 rows per workgroup");
+  constexpr int kSlots = kMThreads / kR;    // threads per row: 32 or 16
+  constexpr int kUnits = 64 / kSlots;       // 16-byte units per thread and split: 2 or 4
+  constexpr int kChunk = 16 / kUnits;       // splits whose loads are in flight together: 8 or 4
   // o_lat of the workgroup's rows as bf16 hi / lo: [row][64 granules of 8],
-  // granule g of row r stored at g ^ r (16 rows: 16 different bank groups)
-  __shared__ __attribute__((aligned(16))) unsigned short lat[2][kMRows * kDLat];
+  // granule g of row r stored at g ^ (r % 16) (16 rows: 16 different bank groups)
+  __shared__ __attribute__((aligned(16))) unsigned short lat[2][kR * kDLat];
 
   // heads x, x + 8, ... run on XCD x; the row groups of a head are consecutive there
   const int xcd = blockIdx.x & 7, seat = blockIdx.x >> 3;
   const int h = (seat / groups) * 8 + xcd;
-  const int r0 = (seat % groups) * kMRows;
+  const int r0 = (seat % groups) * kR;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
@@ -70,13 +78,12 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
       wa[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 32 * kk));
   }
 
-  // ---- 1: weighted sum over splits; thread = (row rl, slot g32), units g32 + 32 k
-  constexpr int kChunk = 8;   // splits whose loads are in flight together
-  const int rl = t >> 5, g32 = t & 31;
+  // ---- 1: weighted sum over splits; thread = (row rl, slot g32), units g32 + kSlots k
+  const int rl = t / kSlots, g32 = t % kSlots;
   const int r = r0 + rl;
-  float acc[2][8];
+  float acc[kUnits][8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+  for (int k = 0; k < kUnits; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
   if (r < rows) {
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
     float mrun = -INFINITY, den = 0.f;
     for (int s0 = 0; s0 < cnt; s0 += kChunk) {
       float lv[kChunk];
-      f16x8 v[kChunk][2];
+      f16x8 v[kChunk][kUnits];
 #pragma unroll
       for (int i = 0; i < kChunk; ++i) {
         const int s = min(s0 + i, cnt - 1);   // past the end: re-read, weight 0
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
         lv[i] = s0 + i < cnt ? part_lse[pr] : -INFINITY;
         const _Float16* src = part_o + pr * kDLat + 8 * g32;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) v[i][k] = __builtin_bit_cast(f16x8, *(const u32x4*)(src + 256 * k));
+        for (int k = 0; k < kUnits; ++k) v[i][k] = __builtin_bit_cast(f16x8, *(const u32x4*)(src + 8 * kSlots * k));
       }
       float cm = lv[0];
 #pragma unroll
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
       const float sc = __builtin_amdgcn_exp2f(mrun - mnew);   // 0 when mrun = -inf
       den *= sc;
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int k = 0; k < kUnits; ++k)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] *= sc;
 #pragma unroll
@@ -118,7 +125,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
         const float wi = __builtin_amdgcn_exp2f(lv[i] - mnew);   // 0 for -inf
         den += wi;
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+        for (int k = 0; k < kUnits; ++k)
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[k][e] += wi * (float)v[i][k][e];
       }
@@ -126,12 +133,12 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < kUnits; ++k)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[k][e] *= inv;
   }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kUnits; ++k) {
     unsigned short hi[8], lo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -144,29 +151,33 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(const _Float16* __rest
       vh[e] = (unsigned int)hi[2 * e] | ((unsigned int)hi[2 * e + 1] << 16);
       vl[e] = (unsigned int)lo[2 * e] | ((unsigned int)lo[2 * e + 1] << 16);
     }
-    const int g = g32 + 32 * k;
-    const int off = rl * kDLat + 8 * (g ^ rl);
+    const int g = g32 + kSlots * k;
+    const int off = rl * kDLat + 8 * (g ^ (rl & 15));
     *(u32x4*)(&lat[0][off]) = vh;
     *(u32x4*)(&lat[1][off]) = vl;
   }
   __syncthreads();
 
-  // ---- 2: D[v, r] over 16 k-steps; B fragment: lane = row (lane % 16),
-  // 8 consecutive latent values from granule 4 kk + lane / 16
-  f32x4 d = {0, 0, 0, 0};
+  // ---- 2: D[v, r] over 16 k-steps per 16-row tile; B fragment: lane = row
+  // (lane % 16), 8 consecutive latent values from granule 4 kk + lane / 16
   const int br = lane & 15;
 #pragma unroll
-  for (int kk = 0; kk < kKSteps; ++kk) {
-    const int off = br * kDLat + 8 * ((4 * kk + (lane >> 4)) ^ br);
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lat[0][off]));
-    const bf16x8 bl = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lat[1][off]));
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bh, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bl, d, 0, 0, 0);
+  for (int rt = 0; rt < kR / 16; ++rt) {
+    f32x4 d = {0, 0, 0, 0};
+    const int row = 16 * rt + br;
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      const int off = row * kDLat + 8 * ((4 * kk + (lane >> 4)) ^ br);
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lat[0][off]));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, *(const u32x4*)(&lat[1][off]));
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bh, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kk], bl, d, 0, 0, 0);
+    }
+    // d[e] is value 16 w + 4 (lane / 16) + e of row r0 + row
+    const int ro = r0 + row;
+    if (ro < rows)
+      *(f32x4*)(out + ((size_t)ro * kHeads + h) * kDV + 16 * w + 4 * (lane >> 4)) = d;
   }
-  // d[e] is value 16 w + 4 (lane / 16) + e of row r0 + lane % 16
-  const int ro = r0 + br;
-  if (ro < rows)
-    *(f32x4*)(out + ((size_t)ro * kHeads + h) * kDV + 16 * w + 4 * (lane >> 4)) = d;
 }
 
 }  // namespace
@@ -175,9 +186,16 @@ hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const Seq
                         const uint16_t* w_uv, float* out, int batch, int q_tokens, int max_chunks,
                         hipStream_t stream) {
   const int rows = batch * q_tokens;
-  const int groups = (rows + kMRows - 1) / kMRows;
-  hipLaunchKernelGGL(merge_kernel, dim3(kHeads * groups), dim3(kMThreads), 0, stream, part_o,
-                     part_lse, seqinfo, w_uv, out, rows, q_tokens, groups, max_chunks);
+  if (rows <= 32) {
+    // 16-row groups: at least one workgroup per CU for 32 rows
+    const int groups = (rows + 15) / 16;
+    hipLaunchKernelGGL(merge_kernel<16>, dim3(kHeads * groups), dim3(kMThreads), 0, stream, part_o, part_lse,
+                       seqinfo, w_uv, out, rows, q_tokens, groups, max_chunks);
+  } else {
+    const int groups = (rows + 31) / 32;
+    hipLaunchKernelGGL(merge_kernel<32>, dim3(kHeads * groups), dim3(kMThreads), 0, stream, part_o, part_lse,
+                       seqinfo, w_uv, out, rows, q_tokens, groups, max_chunks);
+  }
   return hipGetLastError();
 }
 
