@@ -94,15 +94,6 @@ __device__ void block_sums(unsigned (&v)[kN], unsigned* sh) {
   __syncthreads();
 }
 
-// ceil(a / b) for a, b < 2^26 from an fp32 estimate (r = 1 / b), corrected
-// to the exact integer in 32-bit products (q b <= a + 6 b < 2^32)
-__device__ __forceinline__ unsigned cdiv_est(unsigned a, unsigned b, float r) {
-  unsigned q = (unsigned)((float)a * r);
-  while (q * b < a) ++q;
-  while (q > 0 && (q - 1) * b >= a) --q;
-  return q;
-}
-
 constexpr int kItemCostTiles = 6;   // per-item fixed cost of the attention pass, in tiles
 
 // The split plan. Every sequence's cached tokens [0, L_b) are cut into pieces
@@ -173,25 +164,32 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   if (search) {
     unsigned lo[kPlanWaves], hi[kPlanWaves];
     bool feas[kPlanWaves];
-    const double tb = (double)total / kMinChunk;   // sum_b lb_b lies in [tb, tb + n_ne]
+    const bool uniform = max_l * n_ne == total;   // every nonempty sequence of length max_l
 #pragma unroll
     for (int k = 0; k < kPlanWaves; ++k) {
-      const double cap = (double)(k + 1) * P;
-      feas[k] = cap >= (double)n_ne;
-      // below tb / cap nothing fits (N >= sum lb / mb); from (tb + n_ne) /
-      // (cap - n_ne) on everything fits (N <= sum lb / mb + n_ne); the
-      // search returns the smallest feasible mb whatever the bracket
-      const double l = floor(tb / cap) - 1.0;
-      unsigned h = max_lb;
-      if (cap > (double)n_ne) {
-        const double u = ceil((tb + (double)n_ne) / (cap - (double)n_ne)) + 1.0;
-        if (u < (double)h) h = (unsigned)u;
+      feas[k] = (long long)(k + 1) * P >= n_ne;
+      lo[k] = hi[k] = max(max_lb, 1u);
+    }
+    if (!uniform) {
+      const double tb = (double)total / kMinChunk;   // sum_b lb_b lies in [tb, tb + n_ne]
+#pragma unroll
+      for (int k = 0; k < kPlanWaves; ++k) {
+        const double cap = (double)(k + 1) * P;
+        // below tb / cap nothing fits (N >= sum lb / mb); from (tb + n_ne) /
+        // (cap - n_ne) on everything fits (N <= sum lb / mb + n_ne); the
+        // search returns the smallest feasible mb whatever the bracket
+        const double l = floor(tb / cap) - 1.0;
+        unsigned h = max_lb;
+        if (cap > (double)n_ne) {
+          const double u = ceil((tb + (double)n_ne) / (cap - (double)n_ne)) + 1.0;
+          if (u < (double)h) h = (unsigned)u;
+        }
+        hi[k] = max(h, 1u);
+        lo[k] = l < 1.0 ? 1u : (l >= (double)hi[k] ? hi[k] : (unsigned)l);
       }
-      hi[k] = max(h, 1u);
-      lo[k] = l < 1.0 ? 1u : (l >= (double)hi[k] ? hi[k] : (unsigned)l);
     }
     __shared__ unsigned lo_sh[kPlanWaves];
-    if (max_l * n_ne == total) {
+    if (uniform) {
       // equal lengths (lb blocks each): n_ne ceil(lb / mb) <= cap exactly when
       // ceil(lb / mb) <= floor(cap / n_ne), i.e. mb >= ceil(lb / floor(cap / n_ne))
 #pragma unroll
@@ -206,13 +204,12 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
       for (;;) {
         bool any = false;
         unsigned mid[kPlanWaves];
-        float rm[kPlanWaves];
+        bool open[kPlanWaves];
 #pragma unroll
         for (int k = 0; k < kPlanWaves; ++k) {
-          const bool open = feas[k] && lo[k] < hi[k];
-          any |= open;
-          mid[k] = open ? lo[k] + (hi[k] - lo[k]) / 2 : hi[k];
-          rm[k] = 1.0f / (float)mid[k];
+          open[k] = feas[k] && lo[k] < hi[k];
+          any |= open[k];
+          mid[k] = open[k] ? lo[k] + (hi[k] - lo[k]) / 2 : hi[k];
         }
         if (!any) break;   // uniform across the wavefront
         // every count fits 32 bits: N(mid) <= N(lo_k) <= k P + n_ne, or n_ne
@@ -221,12 +218,14 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
         for (int b = t; b < batch; b += 64) {
           const unsigned lb = ((unsigned)s_len[b] + kMinChunk - 1) / kMinChunk;
 #pragma unroll
-          for (int k = 0; k < kPlanWaves; ++k) cnt[k] += cdiv_est(lb, mid[k], rm[k]);
+          for (int k = 0; k < kPlanWaves; ++k)
+            if (open[k]) cnt[k] += (lb + mid[k] - 1) / mid[k];   // only the searches still open
         }
 #pragma unroll
         for (int k = 0; k < kPlanWaves; ++k) {
+          if (!open[k]) continue;
           const unsigned n = wave_reduce<false>(cnt[k]);
-          if (feas[k] && lo[k] < hi[k]) {
+          {
             if ((double)n <= (double)(k + 1) * P)
               hi[k] = mid[k];
             else
@@ -238,7 +237,7 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
 #pragma unroll
         for (int k = 0; k < kPlanWaves; ++k) lo_sh[k] = lo[k];
     }
-    if (max_l * n_ne != total) {
+    if (!uniform) {
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < kPlanWaves; ++k) lo[k] = hi[k] = lo_sh[k];
