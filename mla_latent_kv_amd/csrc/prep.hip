@@ -478,14 +478,15 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
 
   const int hg = h >> 5, hj = h & 31;
   const int c0 = cb * 128 + 32 * w;           // first latent column of this wave
-  for (int r0 = 0; r0 < rows; r0 += 32) {
+  // row tiles of 32 in pairs, two tiles' loads in flight: tile i + 2 loads
+  // into the buffer tile i just used, under tile i's stores
+  auto tile = [&](int r0, u32x4 (&bt)[8]) {
     const int r = r0 + (lane & 31);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, bq[ks]), acc,
-                                                    0, 0, 0);
-    if (r0 + 32 < rows) load_q(r0 + 32, bq);   // next 32 rows in flight under the stores
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, bt[ks]), acc, 0, 0, 0);
+    if (r0 + 64 < rows) load_q(r0 + 64, bt);
     if (r < rows) {
       // acc[4 q + e] holds column c0 + 8 q + 4 half + e of row r
 #pragma unroll
@@ -497,6 +498,12 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
         *(f16x4*)(q_abs + frag * 8 + (c & 7)) = v;
       }
     }
+  };
+  u32x4 bq2[8];
+  if (32 < rows) load_q(32, bq2);
+  for (int r0 = 0; r0 < rows; r0 += 64) {
+    tile(r0, bq);
+    if (r0 + 32 < rows) tile(r0 + 32, bq2);
   }
 }
 
