@@ -158,3 +158,17 @@ def test_rows_that_see_nothing_are_zero():
     got = run_gpu(batch)
     assert np.all(got[1] == 0.0) and np.all(got[0, 0] == 0.0)
     assert_parity(got, oracle(batch), spec.name)
+
+
+@pytest.mark.parametrize("sq", [1, 2])
+def test_one_item_longer_than_a_block_table_window(sq):
+    """A split target of 1 makes the whole 20,000-token history one work item
+    (313 cache blocks): the attention pass reloads its window of 64 block ids
+    four times within the item. Every head against the oracle (absorb order,
+    itself pinned to the naive definition)."""
+    spec = synth.Spec(f"long_item_sq{sq}", 1, sq, (20000 + sq - 1,))
+    batch = synth.make_batch(spec, seed=31 + sq)
+    say(f"case {spec.name}: one item of {int(batch['seq_lens'][0])} tokens")
+    got = run_gpu(batch, split_target=1)
+    ref = oracle(batch, path="absorb")
+    assert_parity(got, ref, spec.name)
