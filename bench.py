@@ -474,7 +474,7 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). Sequences shard across GPUs with no exchange; run one process "
               "per GPU instead.", file=sys.stderr)
         return 2

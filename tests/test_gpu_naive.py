@@ -6,7 +6,7 @@ Cases: prefill (every prompt token a query, Sq = L) at sizes that span
 several 128-token expansion tiles, 256-query attention tiles and 64-key tiles
 with ragged tails; chunked prefill (Sq < L); rows that see nothing (L < Sq);
 decode-shaped batches, also against the absorbed decode on the GPU; and the
-prompt length 4096 on sampled heads. Bar: the benchmark spec's tolerance
+prompt length 4096 on sampled heads. Bar: the decode's parity tolerance
 (max|err| <= 1e-2 max|ref|, sum|err| / sum|ref| <= 2e-3).
 """
 
