@@ -9,6 +9,8 @@ merge with the W_UV product. Inputs are resident in HBM before the timed
 region; consecutive steps rotate over several independent copies of the
 inputs (each ~188 MB, together well past the 256 MB Infinity Cache) so that
 every step streams its cache from HBM, as successive layers of a model do.
+The default warm-up (1000 steps, ~75 ms) outlasts the clock ramp the GPU
+goes through after idle, so the timed steps run at the steady rate.
 
 Prints one JSON line (see the keys below). Per-kernel durations come from HIP
 events the library records between its launches (mla_decode_run_profiled);
@@ -85,7 +87,7 @@ def copy_probe(mib: int) -> int:
 
 def _hip():
     lib = ctypes.CDLL("libamdhip64.so")
-    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
     lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
@@ -93,12 +95,18 @@ def _hip():
     return lib
 
 
+# hipEventDisableSystemFence: the event's record skips the system-scope fence
+# (an L2 writeback and invalidate), which would otherwise slow the kernel after
+# it; these events only time, and are read after a device synchronisation
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 def _events(hip, n):
     evs = []
     for _ in range(n):
         e = ctypes.c_void_p()
-        if hip.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         evs.append(e)
     return evs
 
@@ -459,8 +467,10 @@ def time_naive(lib, dec, d, B, Sq, stream, args, absorb_ms) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # the GPU's clock settles over the first ~300 steps after idle (122 -> 72 us
+    # per step); 1000 warm-up steps (~75 ms) put the timed steps past that ramp
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", type=int, default=1, help="workload index (0-4)")
     ap.add_argument("--sets", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
