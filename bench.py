@@ -45,9 +45,10 @@ QPROJ_WEIGHT_BYTES = (1536 * 7168 + 128 * 192 * 1536) * 2   # W_DQ and W_UQ, bf1
 # HBM traffic of one attention launch from two rocprofv3 --pmc runs of this
 # script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
 # the same counter reads for a plain device copy of known size (--copy-probe).
-# The figures belong to the attention source they were taken on: when the
-# source hash differs, traffic is reported as null.
-ATTN_TRAFFIC = {"src_sha256": "1368b85e54993382948c22110133e4167e20f71ee9ea2df179f8751659d45340",
+# The figures belong to the workload and the attention source they were taken
+# on: for another workload, or when the source hash differs, traffic is null.
+ATTN_TRAFFIC = {"workload": "uniform_b32_l4096",
+                "src_sha256": "1368b85e54993382948c22110133e4167e20f71ee9ea2df179f8751659d45340",
                 "fetch_kib": 76243.167, "write_kib": 32896.0,
                 "fetch_scale": 1.99994, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
@@ -62,9 +63,9 @@ def attn_source_hash() -> str:
     return h.hexdigest()
 
 
-def attn_traffic():
+def attn_traffic(workload: str):
     t = ATTN_TRAFFIC
-    if not t or t["src_sha256"] != attn_source_hash():
+    if not t or t["workload"] != workload or t["src_sha256"] != attn_source_hash():
         return None
     return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
 
@@ -606,7 +607,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": attn_traffic(),
+            "traffic": attn_traffic(spec.name),
             "algorithmic_bytes_per_launch": work["cache_bytes"],
             "mfma_TFLOPs": work["attn_flops"] / attn_s / 1e12,
             "mfma_frac": work["attn_flops"] / attn_s / 1e12 / MFMA_PEAK_TFLOPS,
