@@ -197,6 +197,8 @@ def absorb_decode(q_nope, q_pe, w_uk, w_uv, c_kv, k_r, scale, return_latent=Fals
     p = np.zeros_like(s)
     for i in range(sq):
         n = visible_len(length, sq, i)
+        if n <= 0:                  # a row that sees no position keeps p = 0: output 0
+            continue
         e = np.exp(s[i, :, :n] - s[i, :, :n].max(axis=1, keepdims=True))
         p[i, :, :n] = e / e.sum(axis=1, keepdims=True)
     o_lat = np.einsum("ihj,jc->ihc", p, c_kv, optimize=True)

@@ -271,6 +271,100 @@ def test_gather_and_block_permutation_invariance():
     assert np.isfinite(o1[0, 0, 1]).all() and np.isfinite(o1[2, 0, 5]).all()
 
 
+PAGED_LENGTHS = (1, 63, 64, 65, 130)
+
+
+def scatter_paged(rows_by_seq, block_size, seed):
+    """Scatter known contiguous rows (uint16 bits, one [L_b, W] array per
+    sequence) into a paged cache, token by token: token j of sequence b goes
+    to physical block table[b, j // block_size], slot j % block_size. The
+    physical blocks are a random permutation (so a table is out of order and
+    sequences interleave), unused slots of a last block hold bf16 NaN and
+    table entries past a sequence's blocks are -1."""
+    rng = np.random.default_rng(seed)
+    width = rows_by_seq[0].shape[1]
+    nblk = [-(-r.shape[0] // block_size) for r in rows_by_seq]
+    total = sum(nblk)
+    perm = rng.permutation(total)
+    cache = np.full((total, block_size, width), synth.BF16_NAN, dtype=np.uint16)
+    table = np.full((len(rows_by_seq), max(nblk)), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[k:k + n]
+        k += n
+    for b, rows in enumerate(rows_by_seq):
+        for j in range(rows.shape[0]):
+            cache[table[b, j // block_size], j % block_size, :] = rows[j]
+    return cache, table
+
+
+def paged_roundtrip_failures(gather, block_size=64, seed=3):
+    """Sequences of PAGED_LENGTHS tokens scattered into one paged cache must
+    come back from ``gather`` exactly (same shape, bit-identical values).
+    Returns the lengths that fail."""
+    rng = np.random.default_rng(seed)
+    known = [synth.f32_to_bf16_bits(rng.standard_normal((L, 576)).astype(np.float32))
+             for L in PAGED_LENGTHS]
+    cache, table = scatter_paged(known, block_size, seed)
+    bad = []
+    for b, L in enumerate(PAGED_LENGTHS):
+        got = gather(cache, table[b], L, block_size)
+        want = orc.bf16_bits_to_f64(known[b])
+        if got.shape != want.shape or not np.array_equal(got, want):
+            bad.append(L)
+    return bad
+
+
+def test_paged_reader_returns_the_scattered_rows_exactly():
+    """The paged reader against known contiguous rows scattered token by token
+    through an out-of-order block table: lengths 1, 63, 64, 65 and 130 (one
+    partial block, one block minus one, exactly one, one plus one, and a
+    partial third block), NaN in every unused slot, -1 table tails. The layout
+    is 576 values per token in 64-token blocks ("DeepSeek-V3" page, MLA cache
+    comparison: 512 + 64 = 576)."""
+    assert paged_roundtrip_failures(orc.gather_sequence) == []
+    assert paged_roundtrip_failures(orc.gather_sequence, block_size=16, seed=4) == []
+
+
+@pytest.mark.parametrize("sq", [1, 2])
+def test_decode_batch_through_the_paged_cache_equals_brute_force(sq):
+    """decode_batch over a paged, permuted, NaN-padded cache equals scalar
+    brute force over the same rows kept contiguous (tiny dims: H=2, d_nope=3,
+    d_rope=2, d_latent=5, d_v=4; lengths 1, 63, 64, 65 and 130 with 64-token
+    blocks), on both of the oracle's paths."""
+    rng = np.random.default_rng(70 + sq)
+    H, dn, dr, dc, dv = 2, 3, 2, 5, 4
+    lens = [max(L, sq) for L in PAGED_LENGTHS]
+    bits = lambda *s: synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+    rows = [bits(L, dc + dr) for L in lens]
+    cache, table = scatter_paged(rows, 64, seed=sq)
+    qn, qp = bits(len(lens), sq, H, dn), bits(len(lens), sq, H, dr)
+    wk, wv = bits(H, dn, dc), bits(H, dv, dc)
+    scale = 1 / math.sqrt(dn + dr)
+    for path in ("naive", "absorb"):
+        got = orc.decode_batch(qn, qp, wk, wv, cache, table, np.array(lens, dtype=np.int32), 64,
+                               scale=scale, path=path)
+        for b, L in enumerate(lens):
+            r = orc.bf16_bits_to_f64(rows[b])
+            want = orc.brute_force_decode(orc.bf16_bits_to_f64(qn[b]), orc.bf16_bits_to_f64(qp[b]),
+                                          orc.bf16_bits_to_f64(wk), orc.bf16_bits_to_f64(wv),
+                                          r[:, :dc], r[:, dc:], scale)
+            assert np.max(np.abs(got[b] - want)) <= 1e-12 * np.max(np.abs(want)), (path, L)
+
+
+def test_absorb_path_rows_that_see_nothing_are_zero():
+    """L < Sq on the absorb-order routine: rows i < Sq - L see no position and
+    are zeros, as on the naive path; the other rows equal the naive path."""
+    rng = np.random.default_rng(64)
+    L, sq = 3, 5
+    qn, qp, wk, wv, c, kr = _full_dims_case(rng, n_heads=2, length=L, sq=sq)
+    scale = orc.default_scale()
+    got = orc.absorb_decode(qn, qp, wk, wv, c, kr, scale)
+    ref = orc.naive_decode(qn, qp, wk, wv, c, kr, scale)
+    assert np.all(got[:sq - L] == 0.0) and np.all(ref[:sq - L] == 0.0)
+    assert np.max(np.abs(got - ref)) <= 1e-10 * np.max(np.abs(ref))
+
+
 def test_bf16_decode_is_exact():
     vals = np.array([0.0, 1.0, -2.5, 3.140625, 1e-3, -65504.0], dtype=np.float32)
     bits = synth.f32_to_bf16_bits(vals)

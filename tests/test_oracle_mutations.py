@@ -120,3 +120,39 @@ def test_rope_half_split_pairing_is_caught(monkeypatch):
     def patch(m):
         m.setattr(orc, "rope_rotate", half_split)
     assert _rope_gap(monkeypatch, patch) > 1e-2
+
+
+# ---- paged reader: a block count rounded down (drops a partial last block)
+# and two full blocks read in swapped order must both fail the round trip of
+# known rows through an out-of-order block table, and the paged decode's
+# agreement with brute force on the same rows kept contiguous
+
+def _gather_floor(cache_bits, table_row, length, block_size):
+    nblk = length // block_size
+    blocks = cache_bits[np.asarray(table_row[:nblk], dtype=np.int64)]
+    rows = blocks.reshape(nblk * block_size, cache_bits.shape[-1])[:length]
+    return orc.bf16_bits_to_f64(rows)
+
+
+def _gather_swapped(cache_bits, table_row, length, block_size):
+    nblk = -(-length // block_size)
+    ids = np.asarray(table_row[:nblk], dtype=np.int64).copy()
+    if nblk >= 2:
+        ids[[0, 1]] = ids[[1, 0]]
+    rows = cache_bits[ids].reshape(nblk * block_size, cache_bits.shape[-1])[:length]
+    return orc.bf16_bits_to_f64(rows)
+
+
+@pytest.mark.parametrize("mutant", [_gather_floor, _gather_swapped], ids=["floor", "swap"])
+def test_paged_reader_mistakes_are_caught(mutant):
+    from tests.test_oracle import paged_roundtrip_failures
+    assert paged_roundtrip_failures(mutant) != []
+
+
+@pytest.mark.parametrize("mutant", [_gather_floor, _gather_swapped], ids=["floor", "swap"])
+def test_paged_reader_mistakes_move_the_paged_decode(monkeypatch, mutant):
+    from tests import test_oracle as t
+    with monkeypatch.context() as m:
+        m.setattr(orc, "gather_sequence", mutant)
+        with pytest.raises((AssertionError, ValueError, IndexError)):
+            t.test_decode_batch_through_the_paged_cache_equals_brute_force(1)
