@@ -1,8 +1,8 @@
 """GPU parity: the HIP library against the fp64 oracle, through the C ABI.
 
-Small batches are compared element by element on every output; the five
-measured workloads at full size are compared on sampled (sequence, head)
-pairs the oracle computes one by one, and checked for finiteness everywhere.
+Every case compares every output: small batches against the naive oracle,
+the four full-size workloads against the oracle's absorb-order routine
+(pinned to the naive definition on the CPU).
 Tolerance: max|err| <= 1e-2 * max|o_ref| and sum|err| / sum|o_ref| <= 2e-3.
 """
 
@@ -39,23 +39,41 @@ def test_tiny_unpaged_config_every_output():
     assert_parity(run_gpu(batch), oracle(batch), spec.name)
 
 
-def _sample(batch, n_pairs, seed):
-    rng = np.random.default_rng(seed)
-    B = batch["seq_lens"].shape[0]
-    bs = rng.choice(B, size=min(B, n_pairs), replace=False)
-    return [(int(b), int(rng.integers(0, 128))) for b in bs] + [(int(bs[0]), 0), (int(bs[-1]), 127)]
-
-
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_full_size_config_sampled(idx):
+def test_full_size_config_every_output(idx):
+    """The four full-size workloads, in the launch configuration the benchmark
+    times (default split target), every output against the oracle's absorb-
+    order routine. That routine is the naive definition regrouped by the
+    identity q^T (U c) = (U^T q)^T c (wq-win.github.io DeepSeek-V3 notes,
+    section 2 algebra check); the CPU tier pins the two together to 1e-10."""
     spec = synth.CONFIGS[idx]
     batch = synth.make_batch(spec, seed=idx)
     say(f"case {spec.name}: B={spec.batch} Sq={spec.q_tokens} tokens={int(batch['seq_lens'].sum())}")
     got = run_gpu(batch)
-    assert np.isfinite(got).all()
-    sample = _sample(batch, 12 if idx != 3 else 4, seed=idx)
-    ref = oracle(batch, sample=sample)
-    assert_parity(got, ref, f"{spec.name} sampled {len(sample)} (b, h)")
+    ref = oracle(batch, path="absorb")
+    assert_parity(got, ref, f"{spec.name} every output")
+
+
+# small batches whose split plan gives each attention workgroup several items
+# in a row (the item loop reuses its LDS rings), partial last blocks
+MULTI_ROUND = [
+    (synth.Spec("rounds_sq1", 8, 1, (100, 1000, 2500, 333, 64, 1500, 777, 2049)), 5),
+    (synth.Spec("rounds_sq2", 6, 2, (97, 1500, 2600, 130, 65, 1025)), 4),
+]
+
+
+@pytest.mark.parametrize("spec,split", MULTI_ROUND, ids=lambda x: getattr(x, "name", str(x)))
+def test_multi_round_plan_every_output(spec, split):
+    from tests import plan_mirror as pm
+    batch = synth.make_batch(spec, seed=41)
+    lens = batch["seq_lens"].tolist()
+    mx = int(batch["max_seq_len"])
+    r = pm.check(lens, mx, split)
+    rounds = -(-r["n_items"] // split)
+    assert rounds >= 2, rounds
+    say(f"case {spec.name}: lens={lens} split {split}: {r['n_items']} items, {rounds} rounds")
+    got = run_gpu(batch, split_target=split)
+    assert_parity(got, oracle(batch), spec.name)
 
 
 def test_block_permutation_is_bitwise_invariant():
