@@ -140,9 +140,24 @@ def copy_bandwidth(mib: int = 1024, reps: int = 5) -> dict:
     return {"bytes_read_and_written": 2 * n, "TBps": 2 * n / s / 1e12}
 
 
-def cpu_baseline(batch, budget_s: float, max_seqs: int) -> dict:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(batch, budget_s: float, max_seqs: int, gpu_out=None) -> dict:
     """The fp64 oracle (naive path) on whole sequences of the batch until the
-    time budget is spent; reported as query tokens per second."""
+    time budget is spent; reported as query tokens per second. Beside it the
+    oracle's absorb-order routine on the whole batch, whose result also checks
+    every output of the timed GPU steps (`gpu_out`, the last timed step's
+    output) against the parity tolerance."""
     from oracle import mla_oracle as orc
     try:
         import threadpoolctl
@@ -161,18 +176,30 @@ def cpu_baseline(batch, budget_s: float, max_seqs: int) -> dict:
             break
     dt = time.perf_counter() - t0
     q = done * batch["q_nope"].shape[1]
+    tokens = int(batch["seq_lens"][:done].sum())
     # the absorb-order routine of the oracle (the GPU path's algorithm, fp64)
     # on the whole batch
     ta = time.perf_counter()
-    orc.decode_batch(batch["q_nope"], batch["q_pe"], batch["w_uk"], batch["w_uv"], batch["cache"],
-                     batch["block_table"], batch["seq_lens"], batch["block_size"], path="absorb")
+    ref = orc.decode_batch(batch["q_nope"], batch["q_pe"], batch["w_uk"], batch["w_uv"], batch["cache"],
+                           batch["block_table"], batch["seq_lens"], batch["block_size"], path="absorb")
     da = time.perf_counter() - ta
     qa = B * batch["q_nope"].shape[1]
-    return {"value": q / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {B} sequences ({done * int(batch['seq_lens'][0])} cached "
-                      f"tokens x 128 heads), fp64 NumPy naive path, {dt:.1f} s",
-            "absorb_order": {"value": qa / da, "unit": "query-tokens/s",
-                             "sample": f"all {B} sequences, fp64 NumPy absorb order, {da:.2f} s"}}
+    out = {"value": q / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu_model": cpu_model(), "blas_threads": int(threads),
+           "sample": f"{done} of {B} sequences ({tokens} cached tokens x 128 heads), "
+                     f"fp64 NumPy naive path, {dt:.1f} s",
+           "absorb_order": {"value": qa / da, "unit": "query-tokens/s",
+                            "sample": f"all {B} sequences, fp64 NumPy absorb order, {da:.2f} s"}}
+    if gpu_out is not None:
+        g = gpu_out.astype(np.float64)
+        err = np.abs(g - ref)
+        max_rel = float(err.max() / np.abs(ref).max())
+        mean_rel = float(err.sum() / np.abs(ref).sum())
+        out["check"] = {"outputs": int(ref.size), "max_rel": max_rel, "mean_rel": mean_rel,
+                        "finite": bool(np.isfinite(g).all()),
+                        "pass": bool(np.isfinite(g).all() and max_rel <= 1e-2 and mean_rel <= 2e-3),
+                        "against": "oracle absorb order, every output of the last timed step"}
+    return out
 
 
 def time_cache_append(lib, dec, d, B, Sq, stream, args) -> dict:
@@ -623,11 +650,19 @@ def main() -> int:
         result["output_project"] = time_output_project(lib, dec, B, Sq, stream, args)
         result["naive"] = time_naive(lib, dec, d, B, Sq, stream, args, ms)
     result["copy_bandwidth"] = copy_bandwidth()
+    rc = 0
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0])
+        # the output of the last timed step (its input set), read back after
+        # every timed region has ended
+        last = outs[(args.steps - 1) % n_sets].cpu().numpy()
+        cb = cpu_baseline(batch, args.cpu_budget, batch["seq_lens"].shape[0], gpu_out=last)
+        result["output_check"] = cb.pop("check")
+        result["cpu_baseline"] = cb
+        if not result["output_check"]["pass"]:
+            rc = 3
     print(json.dumps(result), flush=True)
     dec.close()
-    return 0
+    return rc
 
 
 if __name__ == "__main__":

@@ -43,9 +43,17 @@
  *
  * Numerics: bf16 inputs are consumed exactly. The absorbed query and the
  * softmax probabilities are rounded to fp16 and the latent tile is converted
- * bf16 -> fp16 for the matrix-core products (exact for |c_KV| in fp16's range,
- * i.e. |c_KV| <= 65504; larger magnitudes saturate). q_pe . k_R runs in bf16.
+ * bf16 -> fp16 for the matrix-core products. q_pe . k_R runs in bf16.
  * Accumulation, the softmax and the split merge are fp32; out is fp32.
+ * Range rules of the fp16 operands (no page states value ranges; these are
+ * preconditions of this implementation):
+ *  - c_KV: converted exactly while |c_KV| <= 65504; a larger magnitude
+ *    saturates to +-65504 (round toward zero), silently.
+ *  - q_abs: stored as fp16 after an exact scaling by 2^-4 (q_pe gets the same
+ *    scaling; the softmax scale undoes it), so |q_abs| <= 1048064 stays
+ *    finite. A larger (or non-finite) value is detected: the call still
+ *    returns MLA_OK (it never synchronises), the output may be inf/NaN, and
+ *    mla_decode_range_flags reports MLA_RANGE_QABS for that workspace.
  *
  * Errors: every call returns an int status (MLA_OK = 0 or a negative code);
  * no C++ exception crosses the ABI. Faults inside kernels surface at the
@@ -139,6 +147,17 @@ int mla_decode_run(const mla_decode_ctx* ctx, const mla_decode_args* args, void*
 int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* args,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]);
+
+/* Range flags of the last decode call that used `workspace` (the q_abs rule
+ * under Numerics above): enqueues a 2 KB device-to-host copy of the flags
+ * region at the start of the workspace on `stream`, synchronises that stream
+ * and sets *flags to 0 or MLA_RANGE_QABS. Call it after mla_decode_run on the
+ * same stream; it is a debugging aid, not needed for a correct result.
+ * Errors: MLA_ERR_INVALID_ARG (NULL ctx or flags), MLA_ERR_WORKSPACE (NULL,
+ * misaligned or under 2 KB), MLA_ERR_HIP. */
+#define MLA_RANGE_QABS 1
+int mla_decode_range_flags(const mla_decode_ctx* ctx, const void* workspace, size_t workspace_bytes,
+                           void* stream, int32_t* flags);
 
 /* ---- Packed weights of the projections -----------------------------------
  *

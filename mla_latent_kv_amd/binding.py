@@ -185,6 +185,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_naive_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaNaiveArgs), ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_naive_run.restype = ctypes.c_int
+    lib.mla_decode_range_flags.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]
+    lib.mla_decode_range_flags.restype = ctypes.c_int
     lib.mla_decode_destroy.argtypes = [ctypes.c_void_p]
     lib.mla_decode_destroy.restype = None
     lib.mla_decode_status_string.argtypes = [ctypes.c_int]
@@ -239,14 +242,31 @@ def _require(t, name, dtypes, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
 
 
+MLA_RANGE_QABS = 1
+
+
+def mla_decode_range_flags(ctx, workspace, stream=None) -> int:
+    """Range flags of the last decode call on ``workspace`` (synchronises the
+    stream): 0, or MLA_RANGE_QABS when a q_abs value was past fp16's range."""
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+    flags = ctypes.c_int32()
+    _check(load_library().mla_decode_range_flags(ctx, workspace.data_ptr(),
+                                                 workspace.numel() * workspace.element_size(),
+                                                 ctypes.c_void_p(s.cuda_stream), ctypes.byref(flags)),
+           "mla_decode_range_flags")
+    return flags.value
+
+
 def mla_decode_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_lens,
-                   max_seq_len: int, out=None, workspace=None, stream=None):
+                   max_seq_len: int, out=None, workspace=None, stream=None, check_range=False):
     """Enqueue one decode step; returns ``out`` (fp32 [B, Sq, 128, 128]).
 
     bf16 tensors may be torch.bfloat16 or 16-bit integer views of the same bits.
     ``workspace``: a uint8 CUDA tensor of at least mla_decode_workspace_size bytes
     (allocated here when None). ``stream``: a torch.cuda.Stream or None for the
-    current stream.
+    current stream. ``check_range``: read the range flags back after the call
+    (synchronises) and raise FloatingPointError when q_abs left fp16's range.
     """
     import torch
     b16 = (torch.bfloat16, torch.int16, torch.uint16)
@@ -285,6 +305,9 @@ def mla_decode_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_len
                                          workspace.numel() * workspace.element_size(),
                                          ctypes.c_void_p(s.cuda_stream)),
            "mla_decode_run")
+    if check_range and mla_decode_range_flags(ctx, workspace, s) & MLA_RANGE_QABS:
+        raise FloatingPointError("mla_decode_run: a q_abs value is past 1048064 (fp16 range after the "
+                                 "2^-4 scaling); the output may hold inf or NaN")
     return out
 
 

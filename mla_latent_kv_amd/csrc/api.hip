@@ -129,7 +129,7 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
       mla::launch_prep(a->seq_lens, a->batch, max_len, target, L.positions, L.depth, L.max_chunks, work,
                        seqinfo, meta,
                        (const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,
-                       stream) != hipSuccess) {
+                       (int*)(ws + L.range), stream) != hipSuccess) {
     status = MLA_ERR_HIP;
   } else {
     mla::AttnArgs aa;
@@ -148,7 +148,7 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
     aa.max_chunks = L.max_chunks;
     aa.positions = L.positions;
     aa.depth = L.depth;
-    aa.scale_log2 = ctx->scale * 1.4426950408889634f;
+    aa.scale_log2 = ctx->scale * 1.4426950408889634f / mla::kQScale;
     if (!mark(2) || mla::launch_attn(aa, stream) != hipSuccess || !mark(3) ||
         mla::launch_merge(part_o, part_lse, seqinfo, (const uint16_t*)a->w_uv, a->out, a->batch,
                           a->q_tokens, L.max_chunks, stream) != hipSuccess ||
@@ -170,6 +170,29 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* a,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]) {
   return run_impl(ctx, a, workspace, workspace_bytes, stream, events);
+}
+
+int mla_decode_range_flags(const mla_decode_ctx* ctx, const void* workspace, size_t workspace_bytes,
+                           void* stream_handle, int32_t* flags) {
+  if (!ctx || !flags) return MLA_ERR_INVALID_ARG;
+  const size_t need = sizeof(int) * mla::kAbsorbGroups;
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  int host[mla::kAbsorbGroups];
+  hipStream_t stream = (hipStream_t)stream_handle;
+  int status = MLA_OK;
+  if (hipMemcpyAsync(host, workspace, need, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    status = MLA_ERR_HIP;
+  } else {
+    int any = 0;
+    for (int i = 0; i < mla::kAbsorbGroups; ++i) any |= host[i] != 0;
+    *flags = any ? MLA_RANGE_QABS : 0;
+  }
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  return status;
 }
 
 int mla_cache_append_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t q_tokens,

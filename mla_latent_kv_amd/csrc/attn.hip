@@ -271,6 +271,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qp[ks]));
   MLA_WAIT_VM(0);
+  // q_pe enters the score scaled by kQScale like q_abs (exact: a power of
+  // two on bf16 values; the products and the softmax scale undo it)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 v = __builtin_bit_cast(u32x4, qp[ks]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float lo = __builtin_bit_cast(float, v[d] << 16) * kQScale;
+      const float hi = __builtin_bit_cast(float, v[d] & 0xffff0000u) * kQScale;
+      v[d] = (__builtin_bit_cast(unsigned int, lo) >> 16) | (__builtin_bit_cast(unsigned int, hi) & 0xffff0000u);
+    }
+    qp[ks] = __builtin_bit_cast(bf16x8, v);
+  }
   // tiles 1 and 2 land under the conversion, scores and softmax of tile 0
   for (int i = 1; i < 3 && i < n_tiles; ++i) fetch_tile(i);
 

@@ -29,6 +29,12 @@ constexpr int kMinChunk = 64;           // split granularity (one cache block)
 constexpr int kMaxBatch = 1000000;      // keeps the plan's packed 21-bit counters exact
 constexpr int kPlanWaves = 4;           // the plan fills the positions at most this many times over
 constexpr int kPlanSortMax = 1024;      // batches up to this size get the searched, sorted plan
+constexpr int kAbsorbGroups = kHeads * (kDLat / 128);   // absorb workgroups: (head, 128-wide latent block)
+// q_abs (fp16) and q_pe enter the score products scaled by 2^-4: exact for
+// both, and it moves fp16's overflow bound for q_abs from 65504 to 2^20 - 2^9.
+// The softmax multiplies the scores back by 2^4 together with its scale.
+constexpr float kQScale = 0.0625f;
+constexpr float kQAbsMax = 1048064.0f;  // 65504 / kQScale
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -57,7 +63,7 @@ struct SeqInfo {
 
 // Byte offsets of each region inside the caller's workspace.
 struct Layout {
-  size_t work, seqinfo, meta, qabs, part_o, part_lse, total;
+  size_t range, work, seqinfo, meta, qabs, part_o, part_lse, total;
   int max_chunks;   // capacity of the partial slots
   int positions;    // work-list positions: the split target rounded up to 8
   int depth;        // work-list entries per position
@@ -87,6 +93,9 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
   L.rows = batch * q_tokens;
   const size_t rows_per_chunk = (size_t)q_tokens * kHeads;
   size_t off = 0;
+  // range flags first, at a fixed offset: one int per absorb workgroup,
+  // written on every call (1 = a q_abs value of its tile outside kQAbsMax)
+  L.range = off;   off = align_up(off + sizeof(int) * kAbsorbGroups, 256);
   L.work = off;    off = align_up(off + sizeof(WorkItem) * (size_t)L.depth * L.positions, 256);
   L.seqinfo = off; off = align_up(off + sizeof(SeqInfo) * batch, 256);
   L.meta = off;    off = align_up(off + 64, 256);
@@ -102,7 +111,7 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
 hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target,
                        int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
-                       hipStream_t stream);
+                       int* range_flags, hipStream_t stream);
 struct AttnArgs {
   const uint16_t* cache;
   const int32_t* block_table;
@@ -119,7 +128,7 @@ struct AttnArgs {
   int max_chunks;
   int positions;      // work-list positions (one workgroup each; two for Sq = 2)
   int depth;          // work-list entries per position
-  float scale_log2;   // softmax scale * log2(e)
+  float scale_log2;   // softmax scale * log2(e) / kQScale (the scores arrive scaled by kQScale)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

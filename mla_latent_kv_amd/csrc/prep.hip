@@ -424,7 +424,8 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
 constexpr int kWStride = 288;   // LDS row stride (bytes) of the W_UK slice: 256 + 32 pad
 
 __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ w_uk,
-                             _Float16* __restrict__ q_abs, int rows, int h, int cb, char* wl) {
+                             _Float16* __restrict__ q_abs, int rows, int h, int cb, char* wl,
+                             int* __restrict__ range_flag) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
@@ -478,6 +479,7 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
 
   const int hg = h >> 5, hj = h & 31;
   const int c0 = cb * 128 + 32 * w;           // first latent column of this wave
+  bool out_of_range = false;                  // a value past kQAbsMax (or not finite)
   // row tiles of 32 in pairs, two tiles' loads in flight: tile i + 2 loads
   // into the buffer tile i just used, under tile i's stores
   auto tile = [&](int r0, u32x4 (&bt)[8]) {
@@ -488,12 +490,15 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, bt[ks]), acc, 0, 0, 0);
     if (r0 + 64 < rows) load_q(r0 + 64, bt);
     if (r < rows) {
-      // acc[4 q + e] holds column c0 + 8 q + 4 half + e of row r
+      // acc[4 q + e] holds column c0 + 8 q + 4 half + e of row r; stored
+      // scaled by kQScale (a power of two: the rounding to fp16 is the same)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) out_of_range |= !(__builtin_fabsf(acc[e]) <= kQAbsMax);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = c0 + 8 * q + 4 * half;
-        f16x4 v = {(_Float16)acc[4 * q], (_Float16)acc[4 * q + 1], (_Float16)acc[4 * q + 2],
-                   (_Float16)acc[4 * q + 3]};
+        f16x4 v = {(_Float16)(acc[4 * q] * kQScale), (_Float16)(acc[4 * q + 1] * kQScale),
+                   (_Float16)(acc[4 * q + 2] * kQScale), (_Float16)(acc[4 * q + 3] * kQScale)};
         const size_t frag = (((size_t)r * 4 + hg) * 32 + (c >> 4)) * 64 + hj + 32 * ((c & 15) >> 3);
         *(f16x4*)(q_abs + frag * 8 + (c & 7)) = v;
       }
@@ -505,6 +510,9 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
     tile(r0, bq);
     if (r0 + 32 < rows) tile(r0 + 32, bq2);
   }
+  // this workgroup's flag, written on every call (no clearing needed)
+  const int any = __syncthreads_or(out_of_range ? 1 : 0);
+  if (t == 0) *range_flag = any ? 1 : 0;
 }
 
 
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     const int32_t* __restrict__ seq_lens, int batch, int max_len, int split_target, int positions, int depth,
     int max_chunks, WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
     int* __restrict__ meta, const uint16_t* __restrict__ q_nope,
-    const uint16_t* __restrict__ w_uk, _Float16* __restrict__ q_abs, int rows) {
+    const uint16_t* __restrict__ w_uk, _Float16* __restrict__ q_abs, int rows, int* __restrict__ range_flags) {
   __shared__ __attribute__((aligned(16))) char wl[kDNope * kWStride];
   static_assert(128 + 6 * 4 * kPlanSortMax <= kDNope * kWStride, "plan scratch fits the LDS buffer");
   if (blockIdx.x == 0) {
@@ -522,7 +530,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     plan_block(seq_lens, batch, max_len, split_target, positions, depth, max_chunks, work, seqinfo, meta, wl);
   } else {
     const int id = blockIdx.x - 1;
-    absorb_block(q_nope, w_uk, q_abs, rows, id >> 2, id & 3, wl);
+    absorb_block(q_nope, w_uk, q_abs, rows, id >> 2, id & 3, wl, range_flags + id);
   }
 }
 
@@ -531,10 +539,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target, int positions,
                        int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL(prep_kernel, dim3(1 + kHeads * (kDLat / 128)), dim3(kPrepThreads), 0, stream,
+                       int* range_flags, hipStream_t stream) {
+  hipLaunchKernelGGL(prep_kernel, dim3(1 + kAbsorbGroups), dim3(kPrepThreads), 0, stream,
                      seq_lens, batch, max_len, split_target, positions, depth, max_chunks, work, seqinfo, meta,
-                     q_nope, w_uk, q_abs, rows);
+                     q_nope, w_uk, q_abs, rows, range_flags);
   return hipGetLastError();
 }
 

@@ -38,8 +38,9 @@ def _device_plan(spec, seed, split_target=0):
     raw = ws.cpu().numpy()
     dec.close()
     n_work = depth * positions
-    work = raw[:n_work * 32].view(np.int32).reshape(n_work, 8)
-    off = _align(n_work * 32)
+    off = _align(4 * 512)   # the range flags (one int per absorb workgroup) come first
+    work = raw[off:off + n_work * 32].view(np.int32).reshape(n_work, 8)
+    off = _align(off + n_work * 32)
     seqinfo = raw[off:off + B * 16].view(np.int32).reshape(B, 4)
     off = _align(off + B * 16)
     meta = raw[off:off + 16].view(np.int32)
