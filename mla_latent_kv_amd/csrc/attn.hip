@@ -43,15 +43,18 @@
 //   in flight). Each lane converts the c_KV granules it fetched from bf16 to
 //   fp16 in place (exact in fp16's range). Rows past the split re-read its
 //   last row, so NaN padding never reaches the latent MFMAs (their zero
-//   softmax weights cancel them; masked scores become -inf with a select). Granules are stored at g ^ sw(row % 8) (a permutation of
-//   the low 3 bits), which keeps the score reads, the transposed reads and
-//   the conversion free of bank conflicts; the fetch addresses apply the
+//   softmax weights cancel them; masked scores become -inf with a select).
+//   Granules are stored under a row-dependent permutation (S(r) below) that
+//   keeps the score reads, the transposed reads and the P buffer free of
+//   bank conflicts on gfx950's 64-bank LDS; the fetch addresses apply the
 //   inverse permutation.
-// * software pipeline, one barrier per tile. Iteration i issues, in one
-//   stream, the latent MFMAs of tile i, the score MFMAs of tile i + 1, the
-//   conversion of tile i + 2 and the fetch of tile i + 3; the softmax of tile
-//   i + 1 runs on the VALU under the second half of tile i's latent MFMAs. The
-//   barrier then publishes P and the converted tile for the next iteration.
+// * software pipeline, one barrier per tile, one MFMA per issue slot.
+//   Iteration i runs phase A, the score chain of tile i + 1 with the fetch of
+//   tile i + 3 and the conversion of tile i + 2 beside it, then phase B, the
+//   latent MFMAs of tile i with the softmax of tile i + 1 cut into small
+//   stages between them. sched_barrier fixes each slot's contents so the
+//   operand reads stay ahead of their MFMAs. The barrier then publishes P and
+//   the converted tile for the next iteration.
 #include "common.h"
 
 namespace mla {
@@ -189,16 +192,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   auto kvb = [&](int i) -> char* { return smem + (i & (kNKv - 1)) * kKvBytes; };
   auto krb = [&](int i) -> char* { return smem + kOffKr + (i % kNKr) * kKrBytes; };
 
-  // ---- fetch plan. c_KV rows are 1 KB; logical granule g of row r is stored
-  // at g ^ sw(r % 8), sw(x) = 3-bit rotate left of x. Fetch j (0..7) of wave w
-  // moves row 4 j + w: LDS slot `lane` of it holds logical granule
-  // lane ^ sw(r % 8), and sw(r % 8) is 2 w + (j % 2). The k_R fetch moves rows
-  // 8 w .. 8 w + 7 (128 B rows, swizzle g ^ (r % 8)): lane holds row
-  // 8 w + lane / 8, slot lane % 8, logical granule (lane % 8) ^ (lane / 8).
-  const unsigned voff_even = 16u * (unsigned)(lane ^ (2 * w));
-  const unsigned voff_odd = 16u * (unsigned)(lane ^ (2 * w + 1));
+  // ---- fetch plan. c_KV rows are 1 KB, 64 granules of 16 bytes; logical
+  // granule g of row r is stored at g ^ S(r), S(r) = sw(r % 8) + 8 ((r / 8) % 2)
+  // with sw(x) the 3-bit rotate left of x (S is a permutation of 0..15 over any
+  // 16 consecutive rows; why, below). Fetch j (0..7) of wave w moves row
+  // 4 j + w: LDS slot `lane` of it holds logical granule lane ^ S(4 j + w),
+  // and S(4 j + w) = 2 w + (j % 2) + 8 ((j / 2) % 2). The k_R fetch moves rows
+  // 8 w .. 8 w + 7 (128 B rows of 8 granules, stored at g ^ ((r / 2) % 8)):
+  // lane holds row 8 w + lane / 8, slot lane % 8, logical granule
+  // (lane % 8) ^ ((4 w + lane / 16) % 8).
+  const unsigned voff_base = 16u * (unsigned)(lane ^ (2 * w));
+  auto voff_kv = [&](int j) { return voff_base ^ (16u * (j & 1)) ^ (128u * ((j >> 1) & 1)); };
   const unsigned voff_kr =
-      (unsigned)((lane >> 3) * kRowBytes + kDLat * 2 + 16 * ((lane & 7) ^ (lane >> 3)));
+      (unsigned)((lane >> 3) * kRowBytes + kDLat * 2 + 16 * ((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)));
   // block ids of this split, 64 per window: lane i holds the id of block
   // blk_base + i; a tile reads its id with one lane read
   const int32_t* btab = p.block_table + (size_t)b * p.max_blocks_per_seq;
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // wave-uniform (scalar address arithmetic)
   auto fetch_kv = [&](const char* src, int i, int j, int valid) {
     const int srow = min(4 * j + w, valid - 1);
-    dma16(kvb(i) + 1024 * (4 * j + w), src + srow * kRowBytes, (j & 1) ? voff_odd : voff_even);
+    dma16(kvb(i) + 1024 * (4 * j + w), src + srow * kRowBytes, voff_kv(j));
   };
   auto fetch_kr = [&](const char* src, int i) {
     dma16(krb(i) + 1024 * w, src + 8 * w * kRowBytes, voff_kr);
@@ -284,44 +290,69 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     }
     qp[ks] = __builtin_bit_cast(bf16x8, v);
   }
+  // the score chain reads qp through inline MFMAs, whose operand hazards the
+  // compiler does not cover: two wait states after the last VALU write
+  asm volatile("s_nop 1" : "+v"(qp[0]), "+v"(qp[1]), "+v"(qp[2]), "+v"(qp[3]));
   // tiles 1 and 2 land under the conversion, scores and softmax of tile 0
   for (int i = 1; i < 3 && i < n_tiles; ++i) fetch_tile(i);
 
-  // ---- per-lane LDS offsets
-  // c_KV swizzle: sw(x) = ((x & 3) << 1) | (x >> 2) for x < 8, a permutation,
-  // so 8 consecutive rows put one logical granule in 8 different bank groups
-  // (score reads), and rows 4 k .. 4 k + 3 put the granule pair {2 m, 2 m + 1}
-  // in 8 different ones (transposed reads); rows are 1 KB apart, so every row
-  // starts in the same bank.
+  // ---- per-lane LDS offsets. gfx950's LDS serves a 16-byte read 16 lanes at
+  // a time across 64 banks; a pass is free of bank conflicts when its 16
+  // addresses fall in 16 different 16-byte bank groups of a 256-byte window
+  // (measured: a 128-byte window, the 32-bank layout, doubles the time of a
+  // score read). S(r) does that for 16 consecutive rows that read one logical
+  // granule (score reads); sw(x) = ((x & 3) << 1) | (x >> 2) also puts the
+  // granule pair {2 m, 2 m + 1} of rows 4 k .. 4 k + 3 in 8 different groups
+  // (transposed reads). Rows are 1 KB apart, so every row starts in the same
+  // bank.
   auto sw = [](int x) { return ((x & 3) << 1) | (x >> 2); };
-  // scores: row = l32, logical granule 2 ks + half; k-step ks reads
-  // s_off[ks % 4] + 128 (ks / 4) (the swizzle only moves the low 3 bits); k_R
-  // k-step ks reads r_off[ks] in the k_R buffer
-  int s_off[4], r_off[4];
+  // scores: row = l32, logical granule 2 ks + half, stored at
+  // l32 * 1024 + 16 ((2 ks + half) ^ S(l32)): the low 3 bits move by sw(l32 % 8)
+  // and the 128-byte block ks / 4 becomes (ks / 4) ^ b3, b3 = (l32 / 8) % 2,
+  // i.e. + b3 for even blocks and - b3 for odd ones (s_at). k_R k-step ks
+  // reads r_off[ks] in the k_R buffer.
+  int s_offE[4], s_offO[4], r_off[4];
+  {
+    const int b3 = (l32 >> 3) & 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s_off[j] = l32 * 1024 + 16 * ((2 * j + half) ^ sw(l32 & 7));
-    r_off[j] = l32 * 128 + 16 * ((2 * j + half) ^ (l32 & 7));
+    for (int j = 0; j < 4; ++j) {
+      const int base = l32 * 1024 + 16 * ((2 * j + half) ^ sw(l32 & 7));
+      s_offE[j] = base + 128 * b3;
+      s_offO[j] = base - 128 * b3;
+      r_off[j] = l32 * 128 + 16 * ((2 * j + half) ^ ((l32 >> 1) & 7));
+    }
   }
+  auto s_at = [&](int ks) { return (((ks >> 2) & 1) ? s_offO : s_offE)[ks & 3] + 128 * (ks >> 2); };
   // transposed reads of this wave's columns. MFMA k-slot (hh, e) of k-step st
   // is token 16 st + 8 (e / 4) + 4 hh + e % 4 (the score accumulator's token
   // order). Group gg = lane / 16 (k-half hh = gg / 2, 16-column half gg % 2);
   // for read q source lane L addresses token 16 st + 8 q + 4 hh + L / 4 at
-  // column 128 w + 32 ct + 16 (gg % 2) + 4 (L % 4). The row swizzle
-  // (sw(row % 8)) is the same for every st and q, so one base per column tile
-  // serves them all (st and q add immediates).
+  // column 128 w + 32 ct + 16 (gg % 2) + 4 (L % 4). For q = 0 the row's
+  // swizzle is sw(row % 8) for every st, so one base per column tile serves
+  // all k-steps; rows of q = 1 add 8 to S, which flips bit 3 of the granule:
+  // bit 6 of the column, i.e. ct / 2 (tr_pair).
   const int gg = lane >> 4, Lq = lane & 15, hh = gg >> 1;
-  int tr_off[4];
+  // the low-3-bit swizzle flips bit 2 of the granule at most, and a column
+  // tile is 4 granules: tiles 2 and 3 sit 8 granules (128 bytes) past tiles 0
+  // and 1, so two registers serve all four (tr_at)
+  int tr_off2[2];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int ct = 0; ct < 2; ++ct) {
     const int row = 4 * hh + (Lq >> 2);
     const int col = kColsPerWave * w + 32 * ct + 16 * (gg & 1) + 4 * (Lq & 3);
-    tr_off[ct] = row * 1024 + 16 * ((col >> 3) ^ sw(row & 7)) + 2 * (col & 7);
+    tr_off2[ct] = row * 1024 + 16 * ((col >> 3) ^ sw(row & 7)) + 2 * (col & 7);
   }
+  auto tr_at = [&](int ct) { return tr_off2[ct & 1] + 128 * (ct >> 1); };
+  // A operand of column tile ct, k-step st, from the tile at `tb`
+  auto tr_pair = [&](const char* tb, int ct, int st) {
+    const char* p0 = tb + tr_at(ct) + 1024 * 16 * st;
+    return lds_read_tr(p0, p0 + 1024 * 8 + ((ct >> 1) ? -128 : 128));
+  };
   // P: [row][32 positions] fp16, 64 B per row, 16-byte chunk c stored at
-  // c ^ ((row / 2) % 4). Position 16 st + 8 hh + e holds the token of k-slot
-  // (hh, e) of k-step st, so a B fragment is one 16-byte chunk (2 st + hh).
-  auto p_chunk = [](int row, int c) { return row * 64 + 16 * (c ^ ((row >> 1) & 3)); };
+  // c ^ ((row / 4) % 4) (16 consecutive rows reading one chunk fill 16 bank
+  // groups). Position 16 st + 8 hh + e holds the token of k-slot (hh, e) of
+  // k-step st, so a B fragment is one 16-byte chunk (2 st + hh).
+  auto p_chunk = [](int row, int c) { return row * 64 + 16 * (c ^ ((row >> 2) & 3)); };
 
   f32x16 o[4][4];   // [column tile][row tile]
 #pragma unroll
@@ -381,9 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   };
 
   // rescale O rows whose reference moved (rare); flags / factors of parity par
-  auto rescale_o = [&](int par) {
-    const int4 fl = *(const int4*)(smem + kOffFlag + par * kWaves * 4);
-    if (fl.x | fl.y | fl.z | fl.w) {
+  auto rescale_o = [&](int par, int4 fl) {
+    {
       const float* al = (const float*)(smem + kOffAlpha + par * kRowsPerWg * 4);
       float ah[4];
 #pragma unroll
@@ -419,8 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     for (int h = 0; h < 4; ++h) pb[h] = lds_read16<f16x8>(pbuf, p_chunk(32 * h + l32, 2 * st + half));
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const f16x8 a = lds_read_tr(cur + tr_off[ct] + 1024 * 16 * st,
-                                  cur + tr_off[ct] + 1024 * (16 * st + 8));
+      const f16x8 a = tr_pair(cur, ct, st);
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         o[ct][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[h], o[ct][h], 0, 0, 0);
@@ -437,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     f32x16 s;
     f16x8 sa[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sa[j] = lds_read16<f16x8>(kv, s_off[j]);
+    for (int j = 0; j < 4; ++j) sa[j] = lds_read16<f16x8>(kv, s_at(j));
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
       if (ks == 0) {
@@ -446,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
         S_MFMA(s, sa[ks & 3], qa[ks]);
       }
       const int nk = ks + 4;
-      if (nk < 32) sa[ks & 3] = lds_read16<f16x8>(kv, s_off[nk & 3] + 128 * (nk >> 2));
+      if (nk < 32) sa[ks & 3] = lds_read16<f16x8>(kv, s_at(nk));
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -475,6 +504,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // i + 3 and the conversion works on the dead buffer of tile i + 2, so no
   // branch splits the stream; all fetches are drained before the epilogue.
   const int t_last = t0 + (n_tiles - 1) * kTileTok;
+  // One issue slot = one MFMA plus the loads, stores and VALU work placed
+  // beside it; sched_barrier keeps every slot's work where it is written, so
+  // the operand loads stay several MFMAs ahead of their use (the compiler
+  // would otherwise pull them next to the MFMA and wait for each one).
+#define MLA_SLOT() __builtin_amdgcn_sched_barrier(0)
   auto iteration = [&](int i) {
     const int ts = t0 + i * kTileTok;
     const char* cur = kvb(i);
@@ -485,31 +519,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     const char* fsrc = tile_src(fts);
     const int fvalid = wi.t_end - fts;
     char* cbuf = kvb(i + 2);
+    // the rescale flags of tile i, read now and tested before its latent
+    // MFMAs (phase B), so the read's latency hides behind the score chain
+    const int4 flags = *(const int4*)(smem + kOffFlag + (i & 1) * kWaves * 4);
 
-    rescale_o(i & 1);
+    // in-place bf16 -> fp16 of granule g (rows 4 g + w) of tile i + 2: its
+    // fetch was issued in the previous iteration, before the nine fetches of
+    // tile i + 3 (vmcnt counts loads in issue order)
+    auto conv_read = [&](int g) -> u32x4 {
+      switch (g) {   // vmcnt takes an immediate
+        case 0: MLA_WAIT_VM(17); break;
+        case 1: MLA_WAIT_VM(16); break;
+        case 2: MLA_WAIT_VM(15); break;
+        case 3: MLA_WAIT_VM(14); break;
+        case 4: MLA_WAIT_VM(13); break;
+        case 5: MLA_WAIT_VM(12); break;
+        case 6: MLA_WAIT_VM(11); break;
+        default: MLA_WAIT_VM(10); break;
+      }
+      return *(const u32x4*)(cbuf + 1024 * (4 * g + w) + 16 * lane);
+    };
+    auto conv_write = [&](int g, u32x4 v) {
+      *(u32x4*)(cbuf + 1024 * (4 * g + w) + 16 * lane) = bf16x8_to_f16x8(v);
+    };
 
-    // phase 1: score chain of tile i + 1 (32 fp16 + 4 bf16 MFMAs, operands
-    // read 4 k-steps ahead) with 8 latent MFMAs of tile i (k-step 0, column
-    // tiles 0 and 1). Conversion of tile i + 2 on a 4-MFMA cadence: group j
-    // converts granule j - 1 two dwords per MFMA (3 MFMAs after its read),
-    // writes it, then waits for fetch j of tile i + 2, reads granule j and
-    // issues fetch j of tile i + 3 (the k_R fetch in group 8).
-    f16x8 pb[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) pb[h] = lds_read16<f16x8>(pbuf, p_chunk(32 * h + l32, half));
-    f16x8 ta = lds_read_tr(cur + tr_off[0], cur + tr_off[0] + 1024 * 8);
+    // ---- phase A: the score chain of tile i + 1 (32 fp16 + 4 bf16 MFMAs,
+    // operands read 4 k-steps ahead). The nine fetches of tile i + 3 go out in
+    // its first slots; then the eight granules of tile i + 2 are converted,
+    // each read 4 slots before it is converted and written back; the last
+    // slots read phase B's first operands.
     auto s_frag = [&](int ks) -> f16x8 {
-      return ks < 32 ? lds_read16<f16x8>(kv1, s_off[ks & 3] + 128 * (ks >> 2))
+      return ks < 32 ? lds_read16<f16x8>(kv1, s_at(ks))
                      : lds_read16<f16x8>(kr1, r_off[ks - 32]);
     };
     f16x8 sa[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sa[j] = s_frag(j);
-    f16x8 ta3;
-    u32x4 cv = {0, 0, 0, 0}, co;
+    MLA_SLOT();
     f32x16 s;
+    u32x4 cv[2];
+    f16x8 pb[4], ta[2];
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
+      // inline MFMAs keep the chain's accumulator in VGPRs (O holds the AGPRs)
       if (ks == 0) {
         S_MFMA_FIRST(s, sa[0], qa[0]);
       } else if (ks < 32) {
@@ -517,48 +569,98 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       } else {
         S_MFMA_BF16(s, __builtin_bit_cast(bf16x8, sa[ks & 3]), qp[ks - 32]);
       }
-      const int nk = ks + 4;
-      if (nk < 36) sa[ks & 3] = s_frag(nk);
-      if ((ks & 1) && ks < 16) {
-        const int u = ks >> 1, ct = u >> 2, h = u & 3;
-        o[ct][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta, pb[h], o[ct][h], 0, 0, 0);
-        if (u == 3) ta = lds_read_tr(cur + tr_off[1], cur + tr_off[1] + 1024 * 8);
-      }
-      if (ks == 32) ta = lds_read_tr(cur + tr_off[2], cur + tr_off[2] + 1024 * 8);
-      if (ks == 34) ta3 = lds_read_tr(cur + tr_off[3], cur + tr_off[3] + 1024 * 8);
-      const int j = ks >> 2, q = ks & 3;
-      if (j >= 1 && q >= 2) {   // convert dwords 2 (q - 2), +1 of granule j - 1
-#pragma unroll
-        for (int d = 2 * (q - 2); d < 2 * (q - 2) + 2; ++d) {
-          const float lo = __builtin_bit_cast(float, cv[d] << 16);
-          const float hi = __builtin_bit_cast(float, cv[d] & 0xffff0000u);
-          co[d] = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-        }
-      }
-      if (q == 3) {
-        if (j >= 1) *(u32x4*)(cbuf + 1024 * (4 * (j - 1) + w) + 16 * lane) = co;
-        MLA_WAIT_VM(8);   // this lane's fetch j of tile i + 2 has landed
-        if (j < 8) {
-          cv = *(const u32x4*)(cbuf + 1024 * (4 * j + w) + 16 * lane);
-          fetch_kv(fsrc, i + 3, j, fvalid);
-        } else {
-          fetch_kr(fsrc, i + 3);
-        }
-      }
+      if (ks + 4 < 36) sa[ks & 3] = s_frag(ks + 4);
+      if (ks < 8) fetch_kv(fsrc, i + 3, ks, fvalid);
+      if (ks == 8) fetch_kr(fsrc, i + 3);
+      // granule g: read in slot 9 + 3 g, converted and written in slot 13 + 3 g
+      if (ks >= 9 && ks <= 30 && (ks - 9) % 3 == 0) cv[((ks - 9) / 3) & 1] = conv_read((ks - 9) / 3);
+      if (ks >= 13 && ks <= 34 && (ks - 13) % 3 == 0) conv_write((ks - 13) / 3, cv[((ks - 13) / 3) & 1]);
+      // phase B's first operands, in the registers the chain's last k-steps free
+      if (ks >= 32) pb[ks - 32] = lds_read16<f16x8>(pbuf, p_chunk(32 * (ks - 32) + l32, half));
+      if (ks == 33) ta[0] = tr_pair(cur, 0, 0);
+      MLA_SLOT();
     }
-    asm volatile("s_nop 15" : "+v"(s));
 
-    // phase 2: the other 24 latent MFMAs of tile i under the softmax of
-    // tile i + 1
+    // ---- phase B: the latent MFMAs of tile i (2 k-steps x 4 column tiles x 4
+    // row tiles) with the softmax of tile i + 1 cut into small stages, about
+    // one per slot, so the VALU work issues under the MFMAs.
+    const int sts = ts + kTileTok;
+    const int par1 = (i + 1) & 1;
+    float mx[4], mt = 0.f, alpha = 1.f, neg_m = 0.f, rsum[2] = {0.f, 0.f};
+    int any_rescale = 0;
+    f16x4 pq[4];
+    // tokens of this lane's k-half below lim; a full tile needs no mask
+    const int nv = lim - sts - 4 * half;
+    const bool full = sts + kTileTok <= lim;   // wave-uniform
+    auto stage = [&](int k) {
+      switch (k) {
+        case 0:
+          // the chain's last MFMA (inline asm: the compiler does not count its
+          // latency) has written s at least 16 wait states before this read
+          asm volatile("s_nop 15" : "+v"(s));
+          if (!full) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      o[2][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta, pb[h], o[2][h], 0, 0, 0);
+            for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3)) < nv ? s[e] : -INFINITY;
+          }
+          break;
+        case 1:
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      o[3][h] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta3, pb[h], o[3][h], 0, 0, 0);
-    pv_step(cur, pbuf, 1);
-    softmax_tile(s, ts + kTileTok, (i + 1) & 1);
+          for (int q = 0; q < 4; ++q) mx[q] = fmaxf(fmaxf(s[4 * q], s[4 * q + 1]), fmaxf(s[4 * q + 2], s[4 * q + 3]));
+          break;
+        case 2: {
+          mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+          const Pair32 pm = pair32(mt);
+          mt = fmaxf(pm.a, pm.b) * scale_log2;
+          break;
+        }
+        case 3: {
+          const bool grow = mt > m + kRescaleLog2;
+          const float m_new = grow ? mt : m;
+          const bool rescale = grow && m != -INFINITY;
+          alpha = rescale ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+          any_rescale = __ballot(rescale) != 0ull;
+          m = m_new;
+          neg_m = (m == -INFINITY) ? 0.f : -m;
+          break;
+        }
+        default:
+          if (k >= 4 && k < 20) {   // one exponential per stage
+            const int e = k - 4;
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, neg_m));
+            rsum[e & 1] += x;
+            pq[e >> 2][e & 3] = (_Float16)x;
+          } else if (k == 20) {
+            const Pair32 ps = pair32(rsum[0] + rsum[1]);
+            l = l * alpha + (ps.a + ps.b);
+          } else if (k == 21) {
+            char* pdst = smem + kOffP + par1 * kPBytes;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *(f16x4*)(pdst + p_chunk(rr, 2 * (q >> 1) + half) + 8 * (q & 1)) = pq[q];
+            ((float*)(smem + kOffAlpha + par1 * kRowsPerWg * 4))[rr] = alpha;
+            ((int*)(smem + kOffFlag + par1 * kWaves * 4))[w] = any_rescale;
+          }
+          break;
+      }
+    };
 
+    if (flags.x | flags.y | flags.z | flags.w) rescale_o(i & 1, flags);
+    MLA_SLOT();
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int st = k >> 4, ct = (k >> 2) & 3, rt = k & 3;
+      o[ct][rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ta[ct & 1], pb[rt], o[ct][rt], 0, 0, 0);
+      // next column tile's transposed operand, 3 MFMAs ahead of its first use
+      if (rt == 1 && k + 3 < 32) {
+        const int nst = (k + 3) >> 4, nct = ((k + 3) >> 2) & 3;
+        ta[nct & 1] = tr_pair(cur, nct, nst);
+      }
+      // P of k-step 1 replaces k-step 0's once its last MFMA has issued
+      if (st == 0 && ct == 3) pb[rt] = lds_read16<f16x8>(pbuf, p_chunk(32 * rt + l32, 2 + half));
+      // softmax stages 0-21 in slots 1-22 (a stage per slot from the second on)
+      if (k >= 1 && k <= 22) stage(k - 1);
+      MLA_SLOT();
+    }
+    MLA_WAIT_VM(9);   // tile i + 2's k_R fetch has landed too (its nine fetches are all in)
     MLA_WAIT_LGKM0();
     MLA_BARRIER();
   };
@@ -566,7 +668,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // last tile: latent pass only
   {
     const int i = n_tiles - 1;
-    rescale_o(i & 1);
+    const int4 fl = *(const int4*)(smem + kOffFlag + (i & 1) * kWaves * 4);
+    if (fl.x | fl.y | fl.z | fl.w) rescale_o(i & 1, fl);
     const char* cur = kvb(i);
     const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
     pv_step(cur, pbuf, 0);
