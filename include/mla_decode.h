@@ -148,6 +148,24 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* ar
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]);
 
+/* mla_decode_run without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a 66 MiB array inside the
+ * library, one per GPU (the GPU holds it while the library is loaded); the
+ * call allocates nothing, launches the same kernels on `stream` and never
+ * synchronises. Its split plan is limited to one round (at most one work item
+ * per attention slot), so it requires batch <= the split target (by default
+ * the compute-unit count for q_tokens = 1, half of it for q_tokens = 2) and a
+ * workspace layout within 66 MiB: about B * Sq * 128 KB of absorbed queries
+ * plus 128 KB * Sq per attention slot of partial states, which covers every
+ * batch of up to 256 sequences (Sq = 1) or 128 (Sq = 2) on a 256-CU GPU.
+ * Anything larger returns MLA_ERR_WORKSPACE before any launch. Every call on
+ * a GPU uses that GPU's one array (calls that may overlap on one GPU race,
+ * whatever their streams); nothing in it needs clearing between calls. Same
+ * arguments, results (up to rounding: the plan may cut the history
+ * differently) and other errors as mla_decode_run. */
+int mla_decode_run_noalloc(const mla_decode_ctx* ctx, const mla_decode_args* args, void* stream);
+
 /* Range flags of the last decode call that used `workspace` (the q_abs rule
  * under Numerics above): enqueues a 2 KB device-to-host copy of the flags
  * region at the start of the workspace on `stream`, synchronises that stream

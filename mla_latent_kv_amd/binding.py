@@ -185,6 +185,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_naive_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaNaiveArgs), ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_naive_run.restype = ctypes.c_int
+    lib.mla_decode_run_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
+    lib.mla_decode_run_noalloc.restype = ctypes.c_int
     lib.mla_decode_range_flags.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]
     lib.mla_decode_range_flags.restype = ctypes.c_int
@@ -308,6 +310,37 @@ def mla_decode_run(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_len
     if check_range and mla_decode_range_flags(ctx, workspace, s) & MLA_RANGE_QABS:
         raise FloatingPointError("mla_decode_run: a q_abs value is past 1048064 (fp16 range after the "
                                  "2^-4 scaling); the output may hold inf or NaN")
+    return out
+
+
+def mla_decode_run_noalloc(ctx, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_lens,
+                           max_seq_len: int, out, stream=None):
+    """mla_decode_run on the library's own per-GPU scratch array (no workspace,
+    nothing allocated by the library); ``out`` is required (fp32 [B, Sq, 128,
+    128]). The same argument checks as mla_decode_run."""
+    import torch
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _require(q_nope, "q_nope", b16, 4)
+    _require(q_pe, "q_pe", b16, 4)
+    _require(w_uk, "w_uk", b16, 3)
+    _require(w_uv, "w_uv", b16, 3)
+    _require(kv_cache, "kv_cache", b16, 3)
+    _require(block_table, "block_table", (torch.int32,), 2)
+    _require(seq_lens, "seq_lens", (torch.int32,), 1)
+    _require(out, "out", (torch.float32,), 4)
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    if (tuple(q_nope.shape[2:]) != (N_HEADS, D_NOPE) or tuple(q_pe.shape) != (B, Sq, N_HEADS, D_ROPE)
+            or tuple(w_uk.shape) != (N_HEADS, D_NOPE, D_LATENT) or tuple(w_uv.shape) != (N_HEADS, D_V, D_LATENT)
+            or tuple(kv_cache.shape[1:]) != (BLOCK, D_LATENT + D_ROPE) or block_table.shape[0] != B
+            or tuple(seq_lens.shape) != (B,) or tuple(out.shape) != (B, Sq, N_HEADS, D_V)):
+        raise ValueError("mla_decode_run_noalloc: shapes as for mla_decode_run")
+    s = stream if stream is not None else torch.cuda.current_stream(q_nope.device)
+    args = MlaDecodeArgs(
+        q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+        kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+        kv_cache.shape[0], B, Sq, block_table.shape[1], int(max_seq_len))
+    _check(load_library().mla_decode_run_noalloc(ctx, ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)),
+           "mla_decode_run_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/mla_decode.h"
@@ -86,8 +87,10 @@ int mla_decode_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t 
 
 namespace {
 
+// one_round: the allocation-free variant's plan (one round of at most one
+// work item per slot, which needs batch <= split target)
 int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspace,
-             size_t workspace_bytes, void* stream_handle, void* const* events) {
+             size_t workspace_bytes, void* stream_handle, void* const* events, bool one_round = false) {
   if (!ctx || !a) return MLA_ERR_INVALID_ARG;
   if (!a->q_nope || !a->q_pe || !a->w_uk || !a->w_uv || !a->kv_cache || !a->block_table ||
       !a->seq_lens || !a->out)
@@ -101,7 +104,8 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
       !aligned16(a->seq_lens) || !aligned16(a->out))
     return MLA_ERR_MISALIGNED;
   const int target = split_target_of(ctx, a->q_tokens);
-  const mla::Layout L = mla::make_layout(a->batch, a->q_tokens, a->max_seq_len, target);
+  if (one_round && a->batch > target) return MLA_ERR_WORKSPACE;
+  const mla::Layout L = mla::make_layout(a->batch, a->q_tokens, a->max_seq_len, target, one_round);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total)
     return MLA_ERR_WORKSPACE;
 
@@ -126,7 +130,8 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
   };
   int status = MLA_OK;
   if (!mark(0) || !mark(1) ||
-      mla::launch_prep(a->seq_lens, a->batch, max_len, target, L.positions, L.depth, L.max_chunks, work,
+      mla::launch_prep(a->seq_lens, a->batch, max_len, target, one_round ? 1 : mla::kPlanWaves, L.positions,
+                       L.depth, L.max_chunks, work,
                        seqinfo, meta,
                        (const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,
                        (int*)(ws + L.range), stream) != hipSuccess) {
@@ -170,6 +175,47 @@ int mla_decode_run_profiled(const mla_decode_ctx* ctx, const mla_decode_args* a,
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* const events[5]) {
   return run_impl(ctx, a, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// ---- allocation-free decode: the workspace lives in a file-scope device
+// array. In host code `scratch` names a host-side stand-in, not the device
+// array: its device address is looked up once per device (with that device
+// current) and only that address is used.
+namespace {
+constexpr size_t kScratchBytes = (size_t)66 << 20;   // 66 MiB per GPU
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the device address of `scratch` on the current device `dev`; nullptr on failure
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int mla_decode_run_noalloc(const mla_decode_ctx* ctx, const mla_decode_args* a, void* stream) {
+  if (!ctx || !a) return MLA_ERR_INVALID_ARG;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
+  if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  void* ws = scratch_address(ctx->device);
+  if (prev != ctx->device) (void)hipSetDevice(prev);
+  if (!ws) return MLA_ERR_HIP;
+  // run_impl rejects a batch above the split target and a layout past the
+  // array (MLA_ERR_WORKSPACE) before anything is launched
+  return run_impl(ctx, a, ws, kScratchBytes, stream, nullptr, true);
 }
 
 int mla_decode_range_flags(const mla_decode_ctx* ctx, const void* workspace, size_t workspace_bytes,

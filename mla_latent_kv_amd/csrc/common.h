@@ -78,14 +78,18 @@ inline int default_split_target(int n_cu, int q_tokens) {
   return q_tokens == 1 ? n_cu : n_cu / 2;
 }
 
-inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_target) {
+// one_round: the plan is limited to one round (max_rounds = 1), which with
+// batch <= split_target always finds a searched plan of at most one item per
+// slot; the work list then needs depth 1 and the partial states split_target
+// slots.
+inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_target, bool one_round = false) {
   Layout L{};
   const int max_blocks = (max_seq_len + kBlock - 1) / kBlock;
   // items: at most kPlanWaves * P on the searched plan, P + B on the simple
   // one (sum_b ceil(L_b / C) <= total / C + B with C >= total / P); either way
   // no more than one per cache block
   L.positions = (split_target + 7) / 8 * 8;
-  L.depth = kPlanWaves + (batch + split_target - 1) / split_target;
+  L.depth = one_round ? 1 : kPlanWaves + (batch + split_target - 1) / split_target;
   long long cap = (long long)L.depth * split_target;
   long long by_len = (long long)batch * max_blocks;
   L.max_chunks = (int)(cap < by_len ? cap : by_len);
@@ -109,7 +113,7 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
 // ---- launchers (each returns hipGetLastError() of its launch)
 // split plan + absorb product (one launch)
 hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target,
-                       int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
+                       int max_rounds, int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
                        int* range_flags, hipStream_t stream);
 struct AttnArgs {

@@ -117,7 +117,7 @@ constexpr int kItemCostTiles = 6;   // per-item fixed cost of the attention pass
 // p % 8, so XCD x runs slots [x P8 / 8, (x + 1) P8 / 8), consecutive items and
 // therefore the pieces of the same sequences, which share one L2.
 __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens, int batch, int max_len,
-                                           int split_target, int positions, int depth, int max_chunks,
+                                           int split_target, int max_rounds, int positions, int depth, int max_chunks,
                                            WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
                                            int* __restrict__ meta, char* shm) {
   const int t = threadIdx.x;
@@ -153,7 +153,8 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   block_sums<1, true>(ml, shs);
   const long long total = (long long)total_sh, n_ne = nm[0], max_l = ml[0];
   auto up64 = [](long long x) { return (x + kMinChunk - 1) / kMinChunk * kMinChunk; };
-  const bool search = total > 0 && batch <= kPlanSortMax && n_ne <= (long long)kPlanWaves * P;
+  // max_rounds (1 .. kPlanWaves) bounds the rounds the search may choose
+  const bool search = total > 0 && batch <= kPlanSortMax && n_ne <= (long long)max_rounds * P;
 
   // The search works in 64-token blocks: lb = ceil(L / 64) < 2^26, and
   // ceil(L / C) = ceil(lb / (C / 64)) for C a multiple of 64, so every count
@@ -167,7 +168,7 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
     const bool uniform = max_l * n_ne == total;   // every nonempty sequence of length max_l
 #pragma unroll
     for (int k = 0; k < kPlanWaves; ++k) {
-      feas[k] = (long long)(k + 1) * P >= n_ne;
+      feas[k] = k < max_rounds && (long long)(k + 1) * P >= n_ne;
       lo[k] = hi[k] = max(max_lb, 1u);
     }
     if (!uniform) {
@@ -517,7 +518,8 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
 
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
-    const int32_t* __restrict__ seq_lens, int batch, int max_len, int split_target, int positions, int depth,
+    const int32_t* __restrict__ seq_lens, int batch, int max_len, int split_target, int max_rounds, int positions,
+    int depth,
     int max_chunks, WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
     int* __restrict__ meta, const uint16_t* __restrict__ q_nope,
     const uint16_t* __restrict__ w_uk, _Float16* __restrict__ q_abs, int rows, int* __restrict__ range_flags) {
@@ -527,7 +529,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     // the plan is a short serial chain of barriers and reductions that must
     // not wait behind the absorb wavefronts sharing its SIMDs
     __builtin_amdgcn_s_setprio(3);
-    plan_block(seq_lens, batch, max_len, split_target, positions, depth, max_chunks, work, seqinfo, meta, wl);
+    plan_block(seq_lens, batch, max_len, split_target, max_rounds, positions, depth, max_chunks, work, seqinfo, meta,
+               wl);
   } else {
     const int id = blockIdx.x - 1;
     absorb_block(q_nope, w_uk, q_abs, rows, id >> 2, id & 3, wl, range_flags + id);
@@ -536,12 +539,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 
 }  // namespace
 
-hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target, int positions,
-                       int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
+hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target, int max_rounds,
+                       int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
                        int* range_flags, hipStream_t stream) {
   hipLaunchKernelGGL(prep_kernel, dim3(1 + kAbsorbGroups), dim3(kPrepThreads), 0, stream,
-                     seq_lens, batch, max_len, split_target, positions, depth, max_chunks, work, seqinfo, meta,
+                     seq_lens, batch, max_len, split_target, max_rounds, positions, depth, max_chunks, work, seqinfo, meta,
                      q_nope, w_uk, q_abs, rows, range_flags);
   return hipGetLastError();
 }

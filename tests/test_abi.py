@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
                         "mla_query_project_workspace_size", "mla_pack_weight",
                         "mla_naive_workspace_size", "mla_naive_run",
                         "mla_project_new_tokens_workspace_size", "mla_project_new_tokens",
-                        "mla_decode_range_flags"}
+                        "mla_decode_range_flags", "mla_decode_run_noalloc"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
