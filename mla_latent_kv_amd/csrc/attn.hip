@@ -509,27 +509,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // the operand loads stay several MFMAs ahead of their use (the compiler
   // would otherwise pull them next to the MFMA and wait for each one).
 #define MLA_SLOT() __builtin_amdgcn_sched_barrier(0)
-  auto iteration = [&](int i) {
+  // Only about four VALU instructions issue under one 32x32x16 MFMA of the
+  // same wave (measured on gfx950: 8 VALU per MFMA take 42-47 cycles instead of
+  // 32), so the VALU work of an iteration (the conversion's 96 instructions,
+  // the softmax's ~90) is spread at most ~4 per slot.
+  auto iteration = [&](int i, const char* fsrc) -> const char* {
     const int ts = t0 + i * kTileTok;
     const char* cur = kvb(i);
     const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
     const char* kv1 = kvb(i + 1);
     const char* kr1 = krb(i + 1);
     const int fts = min(ts + 3 * kTileTok, t_last);
-    const char* fsrc = tile_src(fts);
     const int fvalid = wi.t_end - fts;
     char* cbuf = kvb(i + 2);
     // the rescale flags of tile i, read now and tested before its latent
     // MFMAs (phase B), so the read's latency hides behind the score chain
     const int4 flags = *(const int4*)(smem + kOffFlag + (i & 1) * kWaves * 4);
 
-    // in-place bf16 -> fp16 of granule g (rows 4 g + w) of tile i + 2: its
-    // fetch was issued in the previous iteration, before the nine fetches of
-    // tile i + 3 (vmcnt counts loads in issue order)
+    // in-place bf16 -> fp16 of granule g (rows 4 g + w) of tile i + 2, read 4
+    // slots before its first dword is converted; its fetch was issued in the
+    // previous iteration, ahead of tile i + 3's fetches (vmcnt counts loads in
+    // issue order; the nine fetches of tile i + 3 go out in slots 0-8, each
+    // before the granule read of its slot), so granule g read in slot 4 g
+    // waits for all but (8 - g) + min(4 g + 1, 9) younger loads
     auto conv_read = [&](int g) -> u32x4 {
       switch (g) {   // vmcnt takes an immediate
-        case 0: MLA_WAIT_VM(17); break;
-        case 1: MLA_WAIT_VM(16); break;
+        case 0: MLA_WAIT_VM(9); break;
+        case 1: MLA_WAIT_VM(12); break;
         case 2: MLA_WAIT_VM(15); break;
         case 3: MLA_WAIT_VM(14); break;
         case 4: MLA_WAIT_VM(13); break;
@@ -539,15 +545,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       }
       return *(const u32x4*)(cbuf + 1024 * (4 * g + w) + 16 * lane);
     };
-    auto conv_write = [&](int g, u32x4 v) {
-      *(u32x4*)(cbuf + 1024 * (4 * g + w) + 16 * lane) = bf16x8_to_f16x8(v);
+    auto conv_dword = [&](u32x4& v, int d) {   // 3 VALU: exact in fp16's range
+      const float lo = __builtin_bit_cast(float, v[d] << 16);
+      const float hi = __builtin_bit_cast(float, v[d] & 0xffff0000u);
+      v[d] = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_pkrtz(lo, hi));
     };
+    auto conv_store = [&](int g, u32x4 v) { *(u32x4*)(cbuf + 1024 * (4 * g + w) + 16 * lane) = v; };
 
     // ---- phase A: the score chain of tile i + 1 (32 fp16 + 4 bf16 MFMAs,
-    // operands read 4 k-steps ahead). The nine fetches of tile i + 3 go out in
-    // its first slots; then the eight granules of tile i + 2 are converted,
-    // each read 4 slots before it is converted and written back; the last
-    // slots read phase B's first operands.
+    // operands read 4 k-steps ahead). Slots 0-8 issue the nine fetches of
+    // tile i + 3; granule g of tile i + 2 is read in slot 4 g, converted a
+    // dword per slot in slots 4 g + 4 .. 4 g + 7 and written back in the last
+    // of them; slots 32-35 read phase B's first operands.
     auto s_frag = [&](int ks) -> f16x8 {
       return ks < 32 ? lds_read16<f16x8>(kv1, s_at(ks))
                      : lds_read16<f16x8>(kr1, r_off[ks - 32]);
@@ -572,9 +581,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       if (ks + 4 < 36) sa[ks & 3] = s_frag(ks + 4);
       if (ks < 8) fetch_kv(fsrc, i + 3, ks, fvalid);
       if (ks == 8) fetch_kr(fsrc, i + 3);
-      // granule g: read in slot 9 + 3 g, converted and written in slot 13 + 3 g
-      if (ks >= 9 && ks <= 30 && (ks - 9) % 3 == 0) cv[((ks - 9) / 3) & 1] = conv_read((ks - 9) / 3);
-      if (ks >= 13 && ks <= 34 && (ks - 13) % 3 == 0) conv_write((ks - 13) / 3, cv[((ks - 13) / 3) & 1]);
+      if (ks < 32 && (ks & 3) == 0) cv[(ks >> 2) & 1] = conv_read(ks >> 2);
+      if (ks >= 4) {
+        const int g = (ks - 4) >> 2, d = (ks - 4) & 3;
+        conv_dword(cv[g & 1], d);
+        if (d == 3) conv_store(g, cv[g & 1]);
+      }
       // phase B's first operands, in the registers the chain's last k-steps free
       if (ks >= 32) pb[ks - 32] = lds_read16<f16x8>(pbuf, p_chunk(32 * (ks - 32) + l32, half));
       if (ks == 33) ta[0] = tr_pair(cur, 0, 0);
@@ -582,69 +594,69 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     }
 
     // ---- phase B: the latent MFMAs of tile i (2 k-steps x 4 column tiles x 4
-    // row tiles) with the softmax of tile i + 1 cut into small stages, about
-    // one per slot, so the VALU work issues under the MFMAs.
+    // row tiles) with the softmax of tile i + 1 cut into stages of at most
+    // about four VALU instructions, one per slot
     const int sts = ts + kTileTok;
     const int par1 = (i + 1) & 1;
     float mx[4], mt = 0.f, alpha = 1.f, neg_m = 0.f, rsum[2] = {0.f, 0.f};
+    bool grow = false, rescale = false;
     int any_rescale = 0;
     f16x4 pq[4];
     // tokens of this lane's k-half below lim; a full tile needs no mask
     const int nv = lim - sts - 4 * half;
     const bool full = sts + kTileTok <= lim;   // wave-uniform
+    auto mx4 = [&](int q) { mx[q] = fmaxf(fmaxf(s[4 * q], s[4 * q + 1]), fmaxf(s[4 * q + 2], s[4 * q + 3])); };
     auto stage = [&](int k) {
-      switch (k) {
-        case 0:
-          // the chain's last MFMA (inline asm: the compiler does not count its
-          // latency) has written s at least 16 wait states before this read
-          asm volatile("s_nop 15" : "+v"(s));
-          if (!full) {
+      if (k == 0) {
+        // the chain's last MFMA (inline asm: the compiler does not count its
+        // latency) has written s at least 16 wait states before this read
+        asm volatile("s_nop 15" : "+v"(s));
+        if (!full) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3)) < nv ? s[e] : -INFINITY;
-          }
-          break;
-        case 1:
-#pragma unroll
-          for (int q = 0; q < 4; ++q) mx[q] = fmaxf(fmaxf(s[4 * q], s[4 * q + 1]), fmaxf(s[4 * q + 2], s[4 * q + 3]));
-          break;
-        case 2: {
-          mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-          const Pair32 pm = pair32(mt);
-          mt = fmaxf(pm.a, pm.b) * scale_log2;
-          break;
+          for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3)) < nv ? s[e] : -INFINITY;
         }
-        case 3: {
-          const bool grow = mt > m + kRescaleLog2;
-          const float m_new = grow ? mt : m;
-          const bool rescale = grow && m != -INFINITY;
-          alpha = rescale ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-          any_rescale = __ballot(rescale) != 0ull;
-          m = m_new;
-          neg_m = (m == -INFINITY) ? 0.f : -m;
-          break;
-        }
-        default:
-          if (k >= 4 && k < 20) {   // one exponential per stage
-            const int e = k - 4;
-            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, neg_m));
-            rsum[e & 1] += x;
-            pq[e >> 2][e & 3] = (_Float16)x;
-          } else if (k == 20) {
-            const Pair32 ps = pair32(rsum[0] + rsum[1]);
-            l = l * alpha + (ps.a + ps.b);
-          } else if (k == 21) {
-            char* pdst = smem + kOffP + par1 * kPBytes;
+      } else if (k == 1) {
+        mx4(0);
+        mx4(1);
+      } else if (k == 2) {
+        mx4(2);
+        mx4(3);
+      } else if (k == 3) {
+        mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      } else if (k == 4) {
+        const Pair32 pm = pair32(mt);
+        mt = fmaxf(pm.a, pm.b) * scale_log2;
+      } else if (k == 5) {
+        grow = mt > m + kRescaleLog2;
+        rescale = grow && m != -INFINITY;
+      } else if (k == 6) {
+        const float m_new = grow ? mt : m;
+        alpha = rescale ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        m = m_new;
+      } else if (k == 7) {
+        any_rescale = __ballot(rescale) != 0ull;
+        neg_m = (m == -INFINITY) ? 0.f : -m;
+      } else if (k >= 8 && k < 24) {   // one exponential per stage
+        const int e = k - 8;
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, neg_m));
+        rsum[e & 1] += x;
+        pq[e >> 2][e & 3] = (_Float16)x;
+      } else if (k == 24) {
+        const Pair32 ps = pair32(rsum[0] + rsum[1]);
+        l = l * alpha + (ps.a + ps.b);
+      } else if (k == 25) {
+        char* pdst = smem + kOffP + par1 * kPBytes;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) *(f16x4*)(pdst + p_chunk(rr, 2 * (q >> 1) + half) + 8 * (q & 1)) = pq[q];
-            ((float*)(smem + kOffAlpha + par1 * kRowsPerWg * 4))[rr] = alpha;
-            ((int*)(smem + kOffFlag + par1 * kWaves * 4))[w] = any_rescale;
-          }
-          break;
+        for (int q = 0; q < 4; ++q) *(f16x4*)(pdst + p_chunk(rr, 2 * (q >> 1) + half) + 8 * (q & 1)) = pq[q];
+      } else if (k == 26) {
+        ((float*)(smem + kOffAlpha + par1 * kRowsPerWg * 4))[rr] = alpha;
+        ((int*)(smem + kOffFlag + par1 * kWaves * 4))[w] = any_rescale;
       }
     };
 
     if (flags.x | flags.y | flags.z | flags.w) rescale_o(i & 1, flags);
     MLA_SLOT();
+    const char* fsrc_next = fsrc;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const int st = k >> 4, ct = (k >> 2) & 3, rt = k & 3;
@@ -656,15 +668,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       }
       // P of k-step 1 replaces k-step 0's once its last MFMA has issued
       if (st == 0 && ct == 3) pb[rt] = lds_read16<f16x8>(pbuf, p_chunk(32 * rt + l32, 2 + half));
-      // softmax stages 0-21 in slots 1-22 (a stage per slot from the second on)
-      if (k >= 1 && k <= 22) stage(k - 1);
+      // softmax stages 0-26 in slots 1-27
+      if (k >= 1 && k <= 27) stage(k - 1);
+      // the next iteration's fetch source (scalar work, off the first slot)
+      if (k == 29) fsrc_next = tile_src(min(ts + 4 * kTileTok, t_last));
       MLA_SLOT();
     }
     MLA_WAIT_VM(9);   // tile i + 2's k_R fetch has landed too (its nine fetches are all in)
     MLA_WAIT_LGKM0();
     MLA_BARRIER();
+    return fsrc_next;
   };
-  for (int i = 0; i + 1 < n_tiles; ++i) iteration(i);
+  {
+    const char* fsrc = tile_src(min(t0 + 3 * kTileTok, t_last));
+    for (int i = 0; i + 1 < n_tiles; ++i) fsrc = iteration(i, fsrc);
+  }
   // last tile: latent pass only
   {
     const int i = n_tiles - 1;
