@@ -130,7 +130,7 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
   };
   int status = MLA_OK;
   if (!mark(0) || !mark(1) ||
-      mla::launch_prep(a->seq_lens, a->batch, max_len, target, one_round ? 1 : mla::kPlanWaves, L.positions,
+      mla::launch_prep(a->seq_lens, a->block_table, a->max_blocks_per_seq, a->num_blocks, a->batch, max_len, target, one_round ? 1 : mla::kPlanWaves, L.positions,
                        L.depth, L.max_chunks, work,
                        seqinfo, meta,
                        (const uint16_t*)a->q_nope, (const uint16_t*)a->w_uk, q_abs, L.rows,

@@ -211,8 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   const int blk_first = wi.t_begin / kBlock;
   const int blk_last = (wi.t_end - 1) / kBlock;
   int blk_base = blk_first;
-  // issued before the query loads below and consumed after them: the wait for
-  // it (the oldest load) does not wait for the queries
+  // issued before the query loads below, consumed from tile 3 on
   int blk_lane = blk_first + lane <= blk_last ? btab[blk_first + lane] : 0;
   auto tile_src = [&](int ts) -> const char* {
     const int bi = ts / kBlock;
@@ -258,13 +257,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qp[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qsrc + 16 * ks));
   }
-  asm volatile("" : "+v"(blk_lane));   // the block ids are in: later waits stay local
 
-  // ---- prologue fetch of tile 0 (tiles 1 and 2 follow once the queries are in)
+  // ---- prologue fetch of tile 0 (tiles 1 and 2 follow once the queries are
+  // in). Tiles 0 and 1 lie in the split's first cache block and tile 2 in
+  // its second (splits start on a block boundary); the plan resolved both
+  // block ids, so these fetches need no block-table round trip.
   const int n_tiles = (wi.t_end - wi.t_begin + kTileTok - 1) / kTileTok;
   const int t0 = wi.t_begin;
   auto fetch_tile = [&](int i) {
-    const char* src = tile_src(t0 + i * kTileTok);
+    const long long blk = i < 2 ? wi.blk0 : wi.blk1;
+    const long long bl = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);   // memory safety
+    const char* src = (const char*)p.cache + ((size_t)bl * kBlock + (i & 1) * kTileTok) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < 8; ++j) fetch_kv(src, i, j, wi.t_end - (t0 + i * kTileTok));
     fetch_kr(src, i);
@@ -277,6 +280,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qp[ks]));
   MLA_WAIT_VM(0);
+  // the block ids (the oldest load) are in as well; the empty asm keeps the
+  // load ahead of this point, so the loop's first lookups do not wait
+  asm volatile("" : "+v"(blk_lane));
   // q_pe enters the score scaled by kQScale like q_abs (exact: a power of
   // two on bf16 values; the products and the softmax scale undo it)
 #pragma unroll

@@ -48,11 +48,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // One split of one sequence: tokens [t_begin, t_end) of sequence b (whose
 // effective length is len); its partial softmax state goes to slot `slot`.
+// blk0 and blk1 are the cache blocks of its first two 64-token blocks (the
+// plan resolves them, so the attention pass can fetch its first tiles
+// without a block-table round trip; blk1 = blk0 when the split has one block).
 // slot < 0 marks an unused entry of the work list. The list is [depth][positions]:
 // the attention workgroup(s) of position p run entries (0, p), (1, p), ... up to
 // the first unused one.
 struct WorkItem {
-  int b, t_begin, t_end, slot, len, pad0, pad1, pad2;
+  int b, t_begin, t_end, slot, len, blk0, blk1, pad;
 };
 
 // Per-sequence split summary written by the plan kernel: partial slots
@@ -112,7 +115,8 @@ inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_ta
 
 // ---- launchers (each returns hipGetLastError() of its launch)
 // split plan + absorb product (one launch)
-hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target,
+hipError_t launch_prep(const int32_t* seq_lens, const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                       int batch, int max_len, int split_target,
                        int max_rounds, int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
                        int* range_flags, hipStream_t stream);

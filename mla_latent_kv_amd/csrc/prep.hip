@@ -15,8 +15,8 @@
 // query side of the identity q^T (U c) = (U^T q)^T c (the algebra check in
 // section 2 of the wq-win.github.io DeepSeek-V3 notes, U = W_UK[h]):
 // transforming the query once lets every cached latent be used as it is. Each
-// absorb workgroup reads its 128 x 128 slice of W_UK once and applies it to
-// every query row of the batch, so W_UK crosses HBM once per call.
+// absorb workgroup reads its 128 x 128 slice of W_UK once and applies it
+// to every query row of the batch, so W_UK crosses HBM once per call.
 //
 // Matrix cores: D[c, r] = sum_k W_UK[h][k][c] * q_nope[r][h][k], bf16 inputs
 // (exact products), fp32 accumulation, 32x32x16 MFMA. W_UK is stored with the
@@ -72,26 +72,15 @@ __device__ __forceinline__ unsigned wave_reduce(unsigned v) {
   return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Workgroup-wide sums (kMax: maxima) of kN 32-bit values per thread: the
-// wavefronts reduce in DPP moves, their results meet in LDS (`sh`: 4 kN
-// entries). Every thread gets the results; all threads must call it.
-template <int kN, bool kMax = false>
-__device__ void block_sums(unsigned (&v)[kN], unsigned* sh) {
-#pragma unroll
-  for (int k = 0; k < kN; ++k) v[k] = wave_reduce<kMax>(v[k]);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0)
-#pragma unroll
-    for (int k = 0; k < kN; ++k) sh[w * kN + k] = v[k];
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kN; ++k) {
-    unsigned r = sh[k];
-#pragma unroll
-    for (int q = 1; q < kPrepThreads / 64; ++q) r = kMax ? (sh[q * kN + k] > r ? sh[q * kN + k] : r) : r + sh[q * kN + k];
-    v[k] = r;
-  }
-  __syncthreads();
+// ceil(x / d) for 32-bit x and d >= 1 through the fp64 reciprocal: the
+// truncated product is the quotient or one below it (x / d < 2^32 and the
+// product's relative error is a few units of 2^-53), and one integer test
+// settles which.
+__device__ __forceinline__ unsigned ceil_div(unsigned x, unsigned d, double inv_d) {
+  const unsigned n = x + d - 1;   // callers keep x + d < 2^32
+  unsigned q = (unsigned)((double)n * inv_d);
+  if ((unsigned long long)(q + 1) * d <= n) ++q;
+  return q;
 }
 
 constexpr int kItemCostTiles = 6;   // per-item fixed cost of the attention pass, in tiles
@@ -116,42 +105,75 @@ constexpr int kItemCostTiles = 6;   // per-item fixed cost of the attention pass
 // (P8 = P rounded up to 8): the attention workgroup at position p runs on XCD
 // p % 8, so XCD x runs slots [x P8 / 8, (x + 1) P8 / 8), consecutive items and
 // therefore the pieces of the same sequences, which share one L2.
-__device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens, int batch, int max_len,
+//
+// The plan is one workgroup's short chain of reductions; it keeps the
+// barriers few (each costs a round trip of every wavefront) and runs the
+// kPlanWaves searches side by side, one per wavefront.
+__device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
+                                           const int32_t* __restrict__ block_table, int mbps, int num_blocks,
+                                           int batch, int max_len,
                                            int split_target, int max_rounds, int positions, int depth, int max_chunks,
                                            WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
                                            int* __restrict__ meta, char* shm) {
+  static_assert(kPlanWaves == kPrepThreads / 64, "one wavefront per searched round count");
   const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
   const int P = split_target;
   const int per_xcd = positions / 8;
   const int per = (batch + kPrepThreads - 1) / kPrepThreads;
   const int b0 = t * per;
   const int b1 = min(batch, b0 + per);
-  unsigned* shs = (unsigned*)shm;                              // sums, 4 x 4 entries
-  unsigned long long* shu = (unsigned long long*)(shm + 64);   // scans, 4 entries
+  // LDS map: [0, 64) totals exchange; [64, 96) scan exchange; [96, 112)
+  // search results; then the per-sequence arrays of the searched plan
+  unsigned* sh_tot = (unsigned*)shm;                          // 4 waves x 4 words
+  unsigned long long* shu = (unsigned long long*)(shm + 64);  // scans, 4 entries
+  unsigned* lo_sh = (unsigned*)(shm + 96);                    // kPlanWaves
+  unsigned* key = (unsigned*)(shm + 128);                     // [kPlanSortMax] sort keys
+  unsigned* skey = key + kPlanSortMax;                        // [kPlanSortMax] keys in sorted order
+  int* s_n = (int*)(skey + kPlanSortMax);                     // per sequence: pieces
+  int* s_base = s_n + kPlanSortMax;                           //   piece length
+  int* s_slot = s_base + kPlanSortMax;                        //   first partial slot
+  int* s_start = s_slot + kPlanSortMax;                       // per sorted entry: first item
+  int* s_len = s_start + kPlanSortMax;                        // lengths (batches up to kPlanSortMax)
   // batches of at most kPlanSortMax keep their lengths in LDS: every later
   // pass (the search's counts above all) reads them there, not from memory
-  int* s_len = (int*)(shm + 128 + 20 * kPlanSortMax);
   const bool cached = batch <= kPlanSortMax;
   for (int b = b0; b < b1 && cached; ++b) s_len[b] = min(max(seq_lens[b], 0), max_len);
   auto len_of = [&](int b) { return cached ? s_len[b] : min(max(seq_lens[b], 0), max_len); };
 
-  // lengths are clamped to [0, max_len] (max_len = min(host bound, block-table reach))
-  long long mine = 0, ne = 0, mx = 0;
+  // ---- totals: sum, nonempty count and maximum of the lengths (clamped to
+  // [0, max_len], max_len = min(host bound, block-table reach)), one barrier.
+  // A thread's sum stays below 2^21 * 2^31 (batch <= kMaxBatch); it is
+  // reduced as two 21-bit-aligned halves, whose wavefront sums fit 32 bits.
+  unsigned long long mine = 0;
+  unsigned ne = 0, mx = 0;
   for (int b = b0; b < b1; ++b) {
-    const long long L = len_of(b);
+    const unsigned L = (unsigned)len_of(b);
     mine += L;
     ne += L > 0;
     mx = L > mx ? L : mx;
   }
-  // the total needs 64 bits: the block scan's inclusive value of the last thread
-  __shared__ unsigned long long total_sh;
-  const unsigned long long inc_total = block_scan((unsigned long long)mine, shu);
-  if (t == kPrepThreads - 1) total_sh = inc_total;
-  unsigned nm[1] = {(unsigned)ne};
-  block_sums<1>(nm, shs);
-  unsigned ml[1] = {(unsigned)mx};
-  block_sums<1, true>(ml, shs);
-  const long long total = (long long)total_sh, n_ne = nm[0], max_l = ml[0];
+  {
+    const unsigned lo21 = wave_reduce<false>((unsigned)(mine & 0x1fffffu));
+    const unsigned hi = wave_reduce<false>((unsigned)(mine >> 21));
+    const unsigned nes = wave_reduce<false>(ne);
+    const unsigned mxs = wave_reduce<true>(mx);
+    if (lane == 0) {
+      sh_tot[4 * wv] = lo21;
+      sh_tot[4 * wv + 1] = hi;
+      sh_tot[4 * wv + 2] = nes;
+      sh_tot[4 * wv + 3] = mxs;
+    }
+  }
+  __syncthreads();
+  unsigned long long total = 0;
+  long long n_ne = 0, max_l = 0;
+#pragma unroll
+  for (int q = 0; q < kPrepThreads / 64; ++q) {
+    total += (unsigned long long)sh_tot[4 * q] + ((unsigned long long)sh_tot[4 * q + 1] << 21);
+    n_ne += sh_tot[4 * q + 2];
+    max_l = max(max_l, (long long)sh_tot[4 * q + 3]);
+  }
   auto up64 = [](long long x) { return (x + kMinChunk - 1) / kMinChunk * kMinChunk; };
   // max_rounds (1 .. kPlanWaves) bounds the rounds the search may choose
   const bool search = total > 0 && batch <= kPlanSortMax && n_ne <= (long long)max_rounds * P;
@@ -163,122 +185,94 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   const unsigned max_lb = (unsigned)((max_l + kMinChunk - 1) / kMinChunk);
   unsigned mb;   // the chosen piece length C = 64 mb
   if (search) {
-    unsigned lo[kPlanWaves], hi[kPlanWaves];
-    bool feas[kPlanWaves];
-    const bool uniform = max_l * n_ne == total;   // every nonempty sequence of length max_l
-#pragma unroll
-    for (int k = 0; k < kPlanWaves; ++k) {
-      feas[k] = k < max_rounds && (long long)(k + 1) * P >= n_ne;
-      lo[k] = hi[k] = max(max_lb, 1u);
-    }
-    if (!uniform) {
+    const bool uniform = max_l * n_ne == (long long)total;   // every nonempty sequence of length max_l
+    auto feasible = [&](int k) { return k < max_rounds && (long long)(k + 1) * P >= n_ne; };
+    // this wavefront's search: round count wv + 1, smallest feasible mb
+    if (!uniform && feasible(wv)) {
       const double tb = (double)total / kMinChunk;   // sum_b lb_b lies in [tb, tb + n_ne]
-#pragma unroll
-      for (int k = 0; k < kPlanWaves; ++k) {
-        const double cap = (double)(k + 1) * P;
-        // below tb / cap nothing fits (N >= sum lb / mb); from (tb + n_ne) /
-        // (cap - n_ne) on everything fits (N <= sum lb / mb + n_ne); the
-        // search returns the smallest feasible mb whatever the bracket
-        const double l = floor(tb / cap) - 1.0;
-        unsigned h = max_lb;
-        if (cap > (double)n_ne) {
-          const double u = ceil((tb + (double)n_ne) / (cap - (double)n_ne)) + 1.0;
-          if (u < (double)h) h = (unsigned)u;
-        }
-        hi[k] = max(h, 1u);
-        lo[k] = l < 1.0 ? 1u : (l >= (double)hi[k] ? hi[k] : (unsigned)l);
+      const double cap = (double)(wv + 1) * P;
+      // below tb / cap nothing fits (N >= sum lb / mb); from (tb + n_ne) /
+      // (cap - n_ne) on everything fits (N <= sum lb / mb + n_ne); the
+      // search returns the smallest feasible mb whatever the bracket
+      const double l = floor(tb / cap) - 1.0;
+      unsigned hi = max_lb;
+      if (cap > (double)n_ne) {
+        const double u = ceil((tb + (double)n_ne) / (cap - (double)n_ne)) + 1.0;
+        if (u < (double)hi) hi = (unsigned)u;
       }
-    }
-    __shared__ unsigned lo_sh[kPlanWaves];
-    if (uniform) {
-      // equal lengths (lb blocks each): n_ne ceil(lb / mb) <= cap exactly when
-      // ceil(lb / mb) <= floor(cap / n_ne), i.e. mb >= ceil(lb / floor(cap / n_ne))
+      hi = max(hi, 1u);
+      unsigned lo = l < 1.0 ? 1u : (l >= (double)hi ? hi : (unsigned)l);
+      // lane i counts sequences i, i + 64, ... (block counts held in VGPRs);
+      // every count fits 32 bits: N(mid) <= N(lo) <= k P + n_ne, or n_ne where
+      // mid is the longest sequence's block count
+      constexpr int kPerLane = kPlanSortMax / 64;
+      unsigned lbv[kPerLane];
 #pragma unroll
-      for (int k = 0; k < kPlanWaves; ++k)
-        if (feas[k]) {
-          const unsigned m = (unsigned)min((long long)(k + 1) * P / n_ne, (long long)max_lb);
-          lo[k] = hi[k] = (max_lb + m - 1) / m;
-        }
-    } else if (t < 64) {
-      // one wavefront runs the kPlanWaves binary searches: lane i counts
-      // sequences i, i + 64, ... and the cross-lane sums take no barrier
-      for (;;) {
-        bool any = false;
-        unsigned mid[kPlanWaves];
-        bool open[kPlanWaves];
-#pragma unroll
-        for (int k = 0; k < kPlanWaves; ++k) {
-          open[k] = feas[k] && lo[k] < hi[k];
-          any |= open[k];
-          mid[k] = open[k] ? lo[k] + (hi[k] - lo[k]) / 2 : hi[k];
-        }
-        if (!any) break;   // uniform across the wavefront
-        // every count fits 32 bits: N(mid) <= N(lo_k) <= k P + n_ne, or n_ne
-        // where mid is the longest sequence's block count
-        unsigned cnt[kPlanWaves] = {};
-        for (int b = t; b < batch; b += 64) {
-          const unsigned lb = ((unsigned)s_len[b] + kMinChunk - 1) / kMinChunk;
-#pragma unroll
-          for (int k = 0; k < kPlanWaves; ++k)
-            if (open[k]) cnt[k] += (lb + mid[k] - 1) / mid[k];   // only the searches still open
-        }
-#pragma unroll
-        for (int k = 0; k < kPlanWaves; ++k) {
-          if (!open[k]) continue;
-          const unsigned n = wave_reduce<false>(cnt[k]);
-          {
-            if ((double)n <= (double)(k + 1) * P)
-              hi[k] = mid[k];
-            else
-              lo[k] = mid[k] + 1;
-          }
-        }
+      for (int j = 0; j < kPerLane; ++j) {
+        const int b = lane + 64 * j;
+        lbv[j] = b < batch ? ((unsigned)s_len[b] + kMinChunk - 1) / kMinChunk : 0u;
       }
-      if (t == 0)
+      const unsigned capu = (unsigned)(wv + 1) * (unsigned)P;
+      while (lo < hi) {   // lo and hi are wavefront-uniform
+        const unsigned mid = lo + (hi - lo) / 2;
+        const double inv = 1.0 / (double)mid;
+        unsigned cnt = 0;
 #pragma unroll
-        for (int k = 0; k < kPlanWaves; ++k) lo_sh[k] = lo[k];
+        for (int j = 0; j < kPerLane; ++j)
+          if (64 * j < batch) cnt += lbv[j] ? ceil_div(lbv[j], mid, inv) : 0u;
+        if (wave_reduce<false>(cnt) <= capu)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      if (lane == 0) lo_sh[wv] = lo;
     }
-    if (!uniform) {
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kPlanWaves; ++k) lo[k] = hi[k] = lo_sh[k];
-    }
+    __syncthreads();
     long long best_cost = -1;
-    mb = hi[kPlanWaves - 1];
+    mb = max(max_lb, 1u);
 #pragma unroll
     for (int k = 0; k < kPlanWaves; ++k) {
-      if (!feas[k]) continue;
-      // k + 1 rounds of items of up to 2 lo tiles (64 lo tokens) each
-      const long long cost = (long long)(k + 1) * (2LL * lo[k] + kItemCostTiles);
+      if (!feasible(k)) continue;
+      unsigned lk;
+      if (uniform) {
+        // equal lengths (lb blocks each): n_ne ceil(lb / mb) <= cap exactly when
+        // ceil(lb / mb) <= floor(cap / n_ne), i.e. mb >= ceil(lb / floor(cap / n_ne))
+        const unsigned m = (unsigned)min((long long)(k + 1) * P / n_ne, (long long)max_lb);
+        lk = (max_lb + m - 1) / m;
+      } else {
+        lk = lo_sh[k];
+      }
+      // k + 1 rounds of items of up to 2 lk tiles (64 lk tokens) each
+      const long long cost = (long long)(k + 1) * (2LL * lk + kItemCostTiles);
       if (best_cost < 0 || cost < best_cost) {
         best_cost = cost;
-        mb = lo[k];
+        mb = lk;
       }
     }
   } else {
     // C = total / P rounded up to 64, no longer than the longest sequence
     // needs (any C of at least max L leaves every sequence one piece)
-    const long long c = max(up64((total + P - 1) / P), (long long)kMinChunk) / kMinChunk;
+    const long long c = max(up64((long long)((total + P - 1) / P)), (long long)kMinChunk) / kMinChunk;
     mb = (unsigned)min(c, (long long)max(max_lb, 1u));
   }
   const long long C = (long long)mb * kMinChunk;
 
   // pieces of a sequence: count n, length `base` (the last one may be shorter)
-  auto pieces = [&](long long L, long long& n, long long& base) {
-    if (L <= 0) {
+  auto pieces = [&](unsigned L, int& n, int& base) {
+    if (L == 0) {
       n = 0;
       base = kMinChunk;
       return;
     }
-    const unsigned lb = ((unsigned)L + kMinChunk - 1) / kMinChunk;
+    const unsigned lb = (L + kMinChunk - 1) / kMinChunk;
     const unsigned nb = (lb + mb - 1) / mb;
     if (search) {
       const unsigned bb = (lb + nb - 1) / nb;   // blocks per piece
-      base = (long long)bb * kMinChunk;
-      n = (lb + bb - 1) / bb;
+      base = (int)(bb * kMinChunk);
+      n = (int)((lb + bb - 1) / bb);
     } else {
-      base = C;
-      n = nb;
+      base = (int)min(C, (long long)0x7fffffff);
+      n = (int)nb;
     }
   };
 
@@ -286,10 +280,10 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   // (the simple plan lists full chunks first)
   unsigned long long cnt = 0;   // n_all | n_full << 21 | n_tail << 42
   for (int b = b0; b < b1; ++b) {
-    const long long L = len_of(b);
-    long long n, base;
+    const unsigned L = (unsigned)len_of(b);
+    int n, base;
     pieces(L, n, base);
-    const long long nf = search ? 0 : L / C;
+    const unsigned nf = search ? 0u : (unsigned)(L / (unsigned long long)C);
     cnt += (unsigned long long)n | ((unsigned long long)nf << 21) | ((unsigned long long)(n - nf) << 42);
   }
   const unsigned long long inc = block_scan(cnt, shu);
@@ -306,96 +300,100 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   }
   const unsigned long long exc = inc - cnt;
 
-  // list entry of item k
-  auto entry = [&](long long k) -> size_t {
-    const int i = (int)(k % P);
-    return (size_t)(k / P) * positions + (size_t)((i % per_xcd) * 8 + i / per_xcd);
+  // list entry of item k (k < n_items < 2^21: 32-bit index arithmetic)
+  auto entry = [&](int k) -> int {
+    const int i = k % P;
+    return (k / P) * positions + (i % per_xcd) * 8 + i / per_xcd;
   };
-  auto put = [&](long long k, int b, long long t0, long long t1, int slot, int L) {
-    if (slot < max_chunks && k / P < depth) work[entry(k)] = WorkItem{b, (int)t0, (int)t1, slot, L, 0, 0, 0};
+  // the cache block holding token tt of sequence b (tt < max_len: inside the
+  // table row), clamped like every cache access
+  auto blk_at = [&](int b, int tt) -> int {
+    const int v = block_table[(size_t)b * mbps + tt / kMinChunk];
+    return v < 0 ? 0 : (v >= num_blocks ? num_blocks - 1 : v);
+  };
+  auto put = [&](int k, int b, int t0, int t1, int slot, int L) {
+    if (slot < max_chunks && k / P < depth) {
+      const int bk0 = blk_at(b, t0);
+      const int bk1 = t1 - t0 > kMinChunk ? blk_at(b, t0 + kMinChunk) : bk0;
+      work[entry(k)] = WorkItem{b, t0, t1, slot, L, bk0, bk1, 0};
+    }
   };
 
   if (!search) {
     int slot = (int)(exc & mask);
-    long long full_idx = (long long)((exc >> 21) & mask);
-    long long tail_idx = tot_full + (long long)((exc >> 42) & mask);
+    int full_idx = (int)((exc >> 21) & mask);
+    int tail_idx = tot_full + (int)((exc >> 42) & mask);
     for (int b = b0; b < b1; ++b) {
-      const long long L = len_of(b);
-      long long n, base;
-      pieces(L, n, base);
-      const long long nf = L / C;
-      seqinfo[b] = SeqInfo{slot, (int)n, (int)L, 0};
-      for (long long q = 0; q < nf; ++q, ++full_idx) put(full_idx, b, q * C, (q + 1) * C, slot + (int)q, (int)L);
-      if (n > nf) put(tail_idx++, b, nf * C, L, slot + (int)nf, (int)L);
-      slot += (int)n;
+      const int L = len_of(b);
+      int n, base;
+      pieces((unsigned)L, n, base);
+      // C may be 2^31 (one piece per sequence); every full chunk ends at or
+      // below L < 2^31
+      const int nf = (int)(L / C);
+      seqinfo[b] = SeqInfo{slot, n, L, 0};
+      for (int q = 0; q < nf; ++q, ++full_idx)
+        put(full_idx, b, (int)(q * C), (int)((q + 1) * C), slot + q, L);
+      if (n > nf) put(tail_idx++, b, (int)(nf * C), L, slot + nf, L);
+      slot += n;
     }
   } else {
-    // sequences ordered longest piece first (ties: lower b first): bitonic
-    // sort of (piece-length bucket, b) keys in LDS, then each item finds its
-    // sequence by binary search over the sorted prefix of item counts
-    unsigned* key = (unsigned*)(shm + 128);                 // [kPlanSortMax]
-    int* s_n = (int*)(shm + 128 + 4 * kPlanSortMax);       // per sequence: pieces
-    int* s_base = s_n + kPlanSortMax;                      //   piece length
-    int* s_slot = s_base + kPlanSortMax;                   //   first partial slot
-    int* s_start = s_slot + kPlanSortMax;                  // per sorted entry: first item
+    // sequences ordered longest piece first (ties: lower b first), then each
+    // item finds its sequence by binary search over the sorted prefix of item
+    // counts
     int slot = (int)(exc & mask);
     for (int b = b0; b < b1; ++b) {
-      const long long L = len_of(b);
-      long long n, base;
-      pieces(L, n, base);
-      seqinfo[b] = SeqInfo{slot, (int)n, (int)L, 0};
-      s_n[b] = (int)n;
-      s_base[b] = (int)base;
+      const int L = s_len[b];
+      int n, base;
+      pieces((unsigned)L, n, base);
+      seqinfo[b] = SeqInfo{slot, n, L, 0};
+      s_n[b] = n;
+      s_base[b] = base;
       s_slot[b] = slot;
-      slot += (int)n;
+      slot += n;
     }
-    int ns = 1;
-    while (ns < batch) ns <<= 1;
     __syncthreads();
     // one round (every slot runs at most one item): sequence order, which
     // keeps a sequence's pieces on one XCD; no sort
     const bool one_round = n_items <= P;
-    for (int q = t; q < ns; q += kPrepThreads) {
-      if (q < batch) {
-        const unsigned bucket = one_round ? 4095u : (unsigned)min(s_base[q] / kMinChunk, 4095);
-        key[q] = ((4095u - bucket) << 20) | (unsigned)q;
-      } else {
-        key[q] = 0xffffffffu;
-      }
-    }
-    __syncthreads();
-    if (!one_round)
-    for (int size = 2; size <= ns; size <<= 1)
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int q = t; q < ns / 2; q += kPrepThreads) {
-          const int a = 2 * q - (q & (stride - 1)), c = a + stride;
-          const unsigned ka = key[a], kc = key[c];
-          if ((ka > kc) == ((a & size) == 0)) {
-            key[a] = kc;
-            key[c] = ka;
-          }
-        }
-        __syncthreads();
-      }
-    // exclusive prefix of item counts in sorted order: thread t owns sorted
-    // entries [e0, e1)
     if (one_round) {
-      // sequence order: a sequence's first item is its first partial slot
-      for (int e = t; e < ns; e += kPrepThreads) s_start[e] = e < batch ? s_slot[e] : n_items;
+      // a sequence's first item is its first partial slot
+      for (int e = t; e < batch; e += kPrepThreads) {
+        skey[e] = (unsigned)e;
+        s_start[e] = s_slot[e];
+      }
     } else {
-      const int eper = (ns + kPrepThreads - 1) / kPrepThreads;
-      const int e0 = min(ns, t * eper), e1 = min(ns, e0 + eper);
+      // rank sort of the distinct keys (bucket of the piece length, b): the
+      // rank of a key is the number of smaller keys
+      for (int q = t; q < batch; q += kPrepThreads)
+        key[q] = ((4095u - (unsigned)min(s_base[q] / kMinChunk, 4095)) << 20) | (unsigned)q;
+      __syncthreads();
+      for (int q = t; q < batch; q += kPrepThreads) {
+        const unsigned kq = key[q];
+        int rank = 0;
+        int j = 0;
+        for (; j + 4 <= batch; j += 4) {
+          const u32x4 k4 = *(const u32x4*)(key + j);
+          rank += (k4[0] < kq) + (k4[1] < kq) + (k4[2] < kq) + (k4[3] < kq);
+        }
+        for (; j < batch; ++j) rank += key[j] < kq;
+        skey[rank] = kq;
+      }
+      __syncthreads();
+      // exclusive prefix of item counts in sorted order: thread t owns sorted
+      // entries [e0, e1)
+      const int eper = (batch + kPrepThreads - 1) / kPrepThreads;
+      const int e0 = min(batch, t * eper), e1 = min(batch, e0 + eper);
       unsigned long long own = 0;
-      for (int e = e0; e < e1; ++e) own += key[e] == 0xffffffffu ? 0 : (unsigned long long)s_n[key[e] & 0xfffffu];
+      for (int e = e0; e < e1; ++e) own += (unsigned long long)s_n[skey[e] & 0xfffffu];
       unsigned long long run = block_scan(own, shu) - own;
       for (int e = e0; e < e1; ++e) {
         s_start[e] = (int)run;
-        run += key[e] == 0xffffffffu ? 0 : (unsigned long long)s_n[key[e] & 0xfffffu];
+        run += (unsigned long long)s_n[skey[e] & 0xfffffu];
       }
     }
     __syncthreads();
     for (int k = t; k < n_items; k += kPrepThreads) {
-      int lo_e = 0, hi_e = ns - 1;   // the last sorted entry with s_start <= k
+      int lo_e = 0, hi_e = batch - 1;   // the last sorted entry with s_start <= k
       while (lo_e < hi_e) {
         const int m = (lo_e + hi_e + 1) >> 1;
         if (s_start[m] <= k)
@@ -403,11 +401,11 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
         else
           hi_e = m - 1;
       }
-      const int b = (int)(key[lo_e] & 0xfffffu);
-      const long long q = k - s_start[lo_e];
-      const long long L = len_of(b);
-      const long long base = s_base[b];
-      put(k, b, q * base, min((q + 1) * base, L), s_slot[b] + (int)q, (int)L);
+      const int b = (int)(skey[lo_e] & 0xfffffu);
+      const int q = k - s_start[lo_e];
+      const int L = s_len[b];
+      const int base = s_base[b];
+      put(k, b, q * base, min((q + 1) * base, L), s_slot[b] + q, L);
     }
   }
   // a position runs its entries up to the first unused one: that entry is
@@ -415,33 +413,50 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
   // earlier call
   for (int pos = t; pos < positions; pos += kPrepThreads) {
     const int i = (pos % 8) * per_xcd + pos / 8;   // the slot at this position
-    const long long count = i < P && n_items > i ? (n_items - 1 - i) / P + 1 : 0;
-    if (count < depth) work[(size_t)count * positions + pos] = WorkItem{0, 0, 0, -1, 0, 0, 0, 0};
+    const int count = i < P && n_items > i ? (n_items - 1 - i) / P + 1 : 0;
+    if (count < depth) work[count * positions + pos] = WorkItem{0, 0, 0, -1, 0, 0, 0, 0};
   }
 }
 
 // ---------------------------------------------------------------- absorb
 
-constexpr int kWStride = 288;   // LDS row stride (bytes) of the W_UK slice: 256 + 32 pad
+constexpr int kAbsCols = 128;                           // latent columns per absorb workgroup (32 per wavefront)
+constexpr int kAbsRowBytes = kAbsCols * 2;              // 256: one k row of the head's W_UK slice
+constexpr int kAbsBytes = kDNope * kAbsRowBytes;        // 32 KB
+static_assert(kAbsorbGroups == kHeads * (kDLat / kAbsCols), "absorb workgroup count");
 
+// LDS byte offset of 16-byte granule g (0..15) of row k of the W_UK slice.
+// Rows are 256 bytes, four 64-byte quarters (32 columns each); quarter q of
+// row k is stored at q ^ (k % 4), so the four consecutive rows a transposing
+// read covers (32 columns each) fill all 64 banks once.
+__device__ __forceinline__ int wl_off(int k, int g) { return k * kAbsRowBytes + 16 * (g ^ (4 * (k & 3))); }
+
+// One absorb workgroup: head h x latent columns [128 cb, 128 cb + 128), every
+// query row; wavefront w owns the 32 columns 128 cb + 32 w + (0..31). Its W_UK
+// slice (32 KB) is read as 256-byte row pieces, and its results fill 16 bytes
+// of each 128-byte line of q_abs (8 consecutive heads x 8 values); the
+// workgroups with the other 7 heads of the line run on the same XCD, so the
+// pieces meet in its L2.
 __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ w_uk,
-                             _Float16* __restrict__ q_abs, int rows, int h, int cb, char* wl,
-                             int* __restrict__ range_flag) {
+                                             _Float16* __restrict__ q_abs, int rows, int h, int cb, char* wl,
+                                             int* __restrict__ range_flag) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-
-  // W_UK[h][k][cb*128 .. +128] -> LDS rows k (16-byte granules, coalesced);
-  // the first 32 query rows' B fragments are loaded in the same round trip
-  const uint16_t* wsrc = w_uk + ((size_t)h * kDNope) * kDLat + cb * 128;
-  u32x4 wv[8];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int G = t + 256 * n;
-    const int k = G >> 4, g = G & 15;
-    wv[n] = *(const u32x4*)(wsrc + (size_t)k * kDLat + g * 8);
-  }
   const int half = lane >> 5;
+
+  // W_UK[h][k][128 cb .. + 128] -> LDS: granule G = t + 256 n is
+  // (k, g) = (G / 16, G % 16); 16 threads per 256-byte row piece
+  constexpr int kWLoads = kAbsBytes / 16 / kPrepThreads;   // 8
+  const uint16_t* wsrc = w_uk + ((size_t)h * kDNope) * kDLat + cb * kAbsCols;
+  u32x4 wv[kWLoads];
+#pragma unroll
+  for (int n = 0; n < kWLoads; ++n) {
+    const int G = t + kPrepThreads * n;
+    wv[n] = *(const u32x4*)(wsrc + (size_t)(G >> 4) * kDLat + 8 * (G & 15));
+  }
+  // B fragments (lane = query row r0 + lane % 32, 8 consecutive k per k-step)
+  // of three 32-row tiles, loaded in the same round trip as the slice
   auto load_q = [&](int r0, u32x4 (&bq)[8]) {
     const int r = r0 + (lane & 31);
 #pragma unroll
@@ -449,103 +464,107 @@ __device__ __forceinline__ void absorb_block(const uint16_t* __restrict__ q_nope
       bq[ks] = r < rows ? *(const u32x4*)(q_nope + ((size_t)r * kHeads + h) * kDNope + 16 * ks + 8 * half)
                         : u32x4{0, 0, 0, 0};
   };
-  u32x4 bq[8];
-  load_q(0, bq);
+  u32x4 bq0[8], bq1[8], bq2[8];
+  load_q(0, bq0);
+  load_q(32, bq1);
+  load_q(64, bq2);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int G = t + 256 * n;
-    const int k = G >> 4, g = G & 15;
-    *(u32x4*)(wl + k * kWStride + g * 16) = wv[n];
+  for (int n = 0; n < kWLoads; ++n) {
+    const int G = t + kPrepThreads * n;
+    *(u32x4*)(wl + wl_off(G >> 4, G & 15)) = wv[n];
   }
   __syncthreads();
 
-  // A fragments (W_UK^T[c][k], lane = c) for all 8 k-steps, via transposing reads.
-  // Lane group gg = lane / 16 covers columns 16 * (gg % 2) + (0..15) and the
-  // k-half hh = gg / 2; source lane L addresses row k = 16 ks + 8 hh + 4 q + L / 4
-  // at column 4 * (L % 4), so the read returns, per lane, 4 consecutive k of its
-  // own column.
+  // A fragments (W_UK^T[c][k], lane = column) of the wavefront's 32 columns
+  // for all 8 k-steps, through transposing reads. Lane group gg = lane / 16
+  // covers columns 32 w + 16 (gg % 2) + (0..15) and the k-half hh = gg / 2;
+  // source lane L addresses row k = 16 ks + 8 hh + 4 q + L / 4 at column
+  // 32 w + 16 (gg % 2) + 4 (L % 4), so the read returns, per lane, 4
+  // consecutive k of its own column.
   const int gg = lane >> 4, L = lane & 15, hh = gg >> 1;
-  const int cw = 32 * w + 16 * (gg & 1) + 4 * (L & 3);
+  const int g = 4 * w + 2 * (gg & 1) + ((L & 3) >> 1);   // granule of the lane's 4 columns
+  const int sub = 8 * (L & 1);                            // byte offset inside it
   bf16x8 a[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    s16x4 p0, p1;
     const int k0 = 16 * ks + 8 * hh + (L >> 2);
-    p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(wl + k0 * kWStride + cw * 2));
-    p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(wl + (k0 + 4) * kWStride + cw * 2));
+    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(wl + wl_off(k0, g) + sub));
+    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(wl + wl_off(k0 + 4, g) + sub));
     a[ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
   const int hg = h >> 5, hj = h & 31;
-  const int c0 = cb * 128 + 32 * w;           // first latent column of this wave
-  bool out_of_range = false;                  // a value past kQAbsMax (or not finite)
-  // row tiles of 32 in pairs, two tiles' loads in flight: tile i + 2 loads
-  // into the buffer tile i just used, under tile i's stores
+  bool out_of_range = false;   // a value past kQAbsMax (or not finite)
+  // one 32-row tile; its buffer then loads the tile three further on
   auto tile = [&](int r0, u32x4 (&bt)[8]) {
     const int r = r0 + (lane & 31);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, bt[ks]), acc, 0, 0, 0);
-    if (r0 + 64 < rows) load_q(r0 + 64, bt);
+    if (r0 + 96 < rows) load_q(r0 + 96, bt);
     if (r < rows) {
-      // acc[4 q + e] holds column c0 + 8 q + 4 half + e of row r; stored
-      // scaled by kQScale (a power of two: the rounding to fp16 is the same)
+      // acc[4 q + e] holds column 128 cb + 32 w + 8 q + 4 half + e of row r;
+      // stored scaled by kQScale (a power of two: the rounding to fp16 is the
+      // same)
 #pragma unroll
       for (int e = 0; e < 16; ++e) out_of_range |= !(__builtin_fabsf(acc[e]) <= kQAbsMax);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int c = c0 + 8 * q + 4 * half;
+        const int c16 = 8 * cb + 2 * w + (q >> 1);   // column / 16
         f16x4 v = {(_Float16)(acc[4 * q] * kQScale), (_Float16)(acc[4 * q + 1] * kQScale),
                    (_Float16)(acc[4 * q + 2] * kQScale), (_Float16)(acc[4 * q + 3] * kQScale)};
-        const size_t frag = (((size_t)r * 4 + hg) * 32 + (c >> 4)) * 64 + hj + 32 * ((c & 15) >> 3);
-        *(f16x4*)(q_abs + frag * 8 + (c & 7)) = v;
+        const size_t frag = (((size_t)r * 4 + hg) * 32 + c16) * 64 + hj + 32 * (q & 1);
+        *(f16x4*)(q_abs + frag * 8 + 4 * half) = v;
       }
     }
   };
-  u32x4 bq2[8];
-  if (32 < rows) load_q(32, bq2);
-  for (int r0 = 0; r0 < rows; r0 += 64) {
-    tile(r0, bq);
-    if (r0 + 32 < rows) tile(r0 + 32, bq2);
+  for (int r0 = 0; r0 < rows; r0 += 96) {
+    tile(r0, bq0);
+    if (r0 + 32 < rows) tile(r0 + 32, bq1);
+    if (r0 + 64 < rows) tile(r0 + 64, bq2);
   }
   // this workgroup's flag, written on every call (no clearing needed)
   const int any = __syncthreads_or(out_of_range ? 1 : 0);
   if (t == 0) *range_flag = any ? 1 : 0;
 }
 
-
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
-    const int32_t* __restrict__ seq_lens, int batch, int max_len, int split_target, int max_rounds, int positions,
-    int depth,
-    int max_chunks, WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table, int mbps, int num_blocks, int batch, int max_len, int split_target, int max_rounds, int positions,
+    int depth, int max_chunks, WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
     int* __restrict__ meta, const uint16_t* __restrict__ q_nope,
     const uint16_t* __restrict__ w_uk, _Float16* __restrict__ q_abs, int rows, int* __restrict__ range_flags) {
-  __shared__ __attribute__((aligned(16))) char wl[kDNope * kWStride];
-  static_assert(128 + 6 * 4 * kPlanSortMax <= kDNope * kWStride, "plan scratch fits the LDS buffer");
+  __shared__ __attribute__((aligned(16))) char wl[kAbsBytes];
+  static_assert(128 + 7 * 4 * kPlanSortMax <= kAbsBytes, "plan scratch fits the LDS buffer");
   if (blockIdx.x == 0) {
     // the plan is a short serial chain of barriers and reductions that must
     // not wait behind the absorb wavefronts sharing its SIMDs
     __builtin_amdgcn_s_setprio(3);
-    plan_block(seq_lens, batch, max_len, split_target, max_rounds, positions, depth, max_chunks, work, seqinfo, meta,
+    plan_block(seq_lens, block_table, mbps, num_blocks, batch, max_len, split_target, max_rounds, positions, depth, max_chunks, work, seqinfo, meta,
                wl);
   } else {
-    const int id = blockIdx.x - 1;
-    absorb_block(q_nope, w_uk, q_abs, rows, id >> 2, id & 3, wl, range_flags + id);
+    // workgroups are dealt to the 8 XCDs round-robin by id (XCD = id % 8):
+    // XCD x takes heads [16 x, 16 x + 16) with all 4 column blocks of each
+    // (seat s: head 16 x + s / 4, column block s % 4), so the 8 heads sharing
+    // a q_abs line and the column blocks sharing q_nope rows meet in one L2
+    const int j = blockIdx.x - 1;
+    const int x = blockIdx.x & 7, s = j >> 3;
+    absorb_block(q_nope, w_uk, q_abs, rows, 16 * x + (s >> 2), s & 3, wl, range_flags + j);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prep(const int32_t* seq_lens, int batch, int max_len, int split_target, int max_rounds,
+hipError_t launch_prep(const int32_t* seq_lens, const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                       int batch, int max_len, int split_target, int max_rounds,
                        int positions, int depth, int max_chunks, WorkItem* work, SeqInfo* seqinfo, int* meta,
                        const uint16_t* q_nope, const uint16_t* w_uk, _Float16* q_abs, int rows,
                        int* range_flags, hipStream_t stream) {
   hipLaunchKernelGGL(prep_kernel, dim3(1 + kAbsorbGroups), dim3(kPrepThreads), 0, stream,
-                     seq_lens, batch, max_len, split_target, max_rounds, positions, depth, max_chunks, work, seqinfo, meta,
-                     q_nope, w_uk, q_abs, rows, range_flags);
+                     seq_lens, block_table, max_blocks_per_seq, num_blocks, batch, max_len, split_target, max_rounds,
+                     positions, depth, max_chunks, work, seqinfo, meta, q_nope, w_uk, q_abs, rows, range_flags);
   return hipGetLastError();
 }
 

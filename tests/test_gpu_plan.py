@@ -68,6 +68,7 @@ def test_device_plan_equals_mirror(name, spec, seed, target):
     say(f"case plan {name}: B={spec.batch} Sq={spec.q_tokens} target={target}")
     batch, work, seqinfo, meta, (P, positions, depth, max_chunks, max_len) = _device_plan(spec, seed, target)
     lens = batch["seq_lens"]
+    table = np.asarray(batch["block_table"])
     pm.check(lens, max_len, P)
     ref = pm.plan(lens, max_len, P, positions, depth, max_chunks)
     say(f"plan {name}: search={ref['search']} C={ref['C']} items={ref['n_items']} "
@@ -80,6 +81,10 @@ def test_device_plan_equals_mirror(name, spec, seed, target):
             e = j * positions + pos
             b, t0, t1, sl = ref["work"][e]
             assert tuple(work[e, :5]) == (b, t0, t1, sl, ref["L"][b]), (name, e)
+            # the cache blocks of the split's first two 64-token blocks
+            blk0 = int(table[b, t0 // 64])
+            blk1 = int(table[b, t0 // 64 + 1]) if t1 - t0 > 64 else blk0
+            assert (int(work[e, 5]), int(work[e, 6])) == (blk0, blk1), (name, e)
             j += 1
         if j < depth:
             assert work[j * positions + pos, 3] == -1, (name, pos, j)
