@@ -75,7 +75,6 @@ constexpr int kOffAlpha = kOffP + 2 * kPBytes;                   // 159744: resc
 constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWg * 4;         // 160768: per-wave flags
 constexpr int kLdsBytes = kOffFlag + 2 * kWaves * 4;             // 160800
 constexpr int kEpiBytes = kWaves * kRowsPerWg * kColsPerWave * 2;   // 131072 transpose space
-constexpr int kOffStat = kOffKr;                                 // 1/l per row, after the loop
 static_assert(kEpiBytes <= kOffKr, "epilogue space is the c_KV ring");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 constexpr float kRescaleLog2 = 15.0f;   // lazy max threshold: p = 2^(x - m) < 2^15
@@ -418,7 +417,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   };
 
   // rescale O rows whose reference moved (rare); flags / factors of parity par
-  auto rescale_o = [&](int par, int4 fl) {
+  // always inlined: an out-of-line copy would take O out of the registers
+  auto rescale_o = [&](int par, int4 fl) __attribute__((always_inline)) {
     {
       const float* al = (const float*)(smem + kOffAlpha + par * kRowsPerWg * 4);
       float ah[4];
@@ -504,11 +504,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   MLA_BARRIER();
 
   // ---- main loop: iteration i = latent pass of tile i, scores and softmax of
-  // tile i + 1, conversion of tile i + 2, fetch of tile i + 3. The body is the
-  // same straight-line MFMA stream for every i: near the end of the split the
-  // fetch re-reads the last tile (an L2 hit) into the free buffer of tile
-  // i + 3 and the conversion works on the dead buffer of tile i + 2, so no
-  // branch splits the stream; all fetches are drained before the epilogue.
+  // tile i + 1, conversion of tile i + 2, fetch of tile i + 3. The body is one
+  // straight-line MFMA stream, compiled three ways: with the fetch and the
+  // conversion, with the conversion only (i = n - 3: tile i + 3 does not
+  // exist) and with neither (i = n - 2), so the last iterations do no dead
+  // work; all fetches are drained before the epilogue.
   const int t_last = t0 + (n_tiles - 1) * kTileTok;
   // One issue slot = one MFMA plus the loads, stores and VALU work placed
   // beside it; sched_barrier keeps every slot's work where it is written, so
@@ -519,7 +519,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // same wave (measured on gfx950: 8 VALU per MFMA take 42-47 cycles instead of
   // 32), so the VALU work of an iteration (the conversion's 96 instructions,
   // the softmax's ~90) is spread at most ~4 per slot.
-  auto iteration = [&](int i, const char* fsrc) -> const char* {
+  // kFetch: tile i + 3 exists; kConv: tile i + 2 exists. Every call passes
+  // constants, so each inlined copy keeps only its own work.
+  auto iteration = [&](int i, const char* fsrc, const bool kFetch, const bool kConv)
+                       __attribute__((always_inline)) -> const char* {
     const int ts = t0 + i * kTileTok;
     const char* cur = kvb(i);
     const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
@@ -537,17 +540,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     // previous iteration, ahead of tile i + 3's fetches (vmcnt counts loads in
     // issue order; the nine fetches of tile i + 3 go out in slots 0-8, each
     // before the granule read of its slot), so granule g read in slot 4 g
-    // waits for all but (8 - g) + min(4 g + 1, 9) younger loads
+    // waits for all but (8 - g) + min(4 g + 1, 9) younger loads; without the
+    // fetch of tile i + 3 only tile i + 2's own later fetches (8 - g) are younger
     auto conv_read = [&](int g) -> u32x4 {
-      switch (g) {   // vmcnt takes an immediate
-        case 0: MLA_WAIT_VM(9); break;
-        case 1: MLA_WAIT_VM(12); break;
-        case 2: MLA_WAIT_VM(15); break;
-        case 3: MLA_WAIT_VM(14); break;
-        case 4: MLA_WAIT_VM(13); break;
-        case 5: MLA_WAIT_VM(12); break;
-        case 6: MLA_WAIT_VM(11); break;
-        default: MLA_WAIT_VM(10); break;
+      if (kFetch) {
+        switch (g) {   // vmcnt takes an immediate
+          case 0: MLA_WAIT_VM(9); break;
+          case 1: MLA_WAIT_VM(12); break;
+          case 2: MLA_WAIT_VM(15); break;
+          case 3: MLA_WAIT_VM(14); break;
+          case 4: MLA_WAIT_VM(13); break;
+          case 5: MLA_WAIT_VM(12); break;
+          case 6: MLA_WAIT_VM(11); break;
+          default: MLA_WAIT_VM(10); break;
+        }
+      } else {
+        switch (g) {
+          case 0: MLA_WAIT_VM(8); break;
+          case 1: MLA_WAIT_VM(7); break;
+          case 2: MLA_WAIT_VM(6); break;
+          case 3: MLA_WAIT_VM(5); break;
+          case 4: MLA_WAIT_VM(4); break;
+          case 5: MLA_WAIT_VM(3); break;
+          case 6: MLA_WAIT_VM(2); break;
+          default: MLA_WAIT_VM(1); break;
+        }
       }
       return *(const u32x4*)(cbuf + 1024 * (4 * g + w) + 16 * lane);
     };
@@ -585,10 +602,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
         S_MFMA_BF16(s, __builtin_bit_cast(bf16x8, sa[ks & 3]), qp[ks - 32]);
       }
       if (ks + 4 < 36) sa[ks & 3] = s_frag(ks + 4);
-      if (ks < 8) fetch_kv(fsrc, i + 3, ks, fvalid);
-      if (ks == 8) fetch_kr(fsrc, i + 3);
-      if (ks < 32 && (ks & 3) == 0) cv[(ks >> 2) & 1] = conv_read(ks >> 2);
-      if (ks >= 4) {
+      if (kFetch && ks < 8) fetch_kv(fsrc, i + 3, ks, fvalid);
+      if (kFetch && ks == 8) fetch_kr(fsrc, i + 3);
+      if (kConv && ks < 32 && (ks & 3) == 0) cv[(ks >> 2) & 1] = conv_read(ks >> 2);
+      if (kConv && ks >= 4) {
         const int g = (ks - 4) >> 2, d = (ks - 4) & 3;
         conv_dword(cv[g & 1], d);
         if (d == 3) conv_store(g, cv[g & 1]);
@@ -677,22 +694,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       // softmax stages 0-26 in slots 1-27
       if (k >= 1 && k <= 27) stage(k - 1);
       // the next iteration's fetch source (scalar work, off the first slot)
-      if (k == 29) fsrc_next = tile_src(min(ts + 4 * kTileTok, t_last));
+      if (kFetch && k == 29) fsrc_next = tile_src(min(ts + 4 * kTileTok, t_last));
       MLA_SLOT();
     }
-    MLA_WAIT_VM(9);   // tile i + 2's k_R fetch has landed too (its nine fetches are all in)
+    // tile i + 2's k_R fetch has landed too (its nine fetches are all in)
+    if (kFetch) {
+      MLA_WAIT_VM(9);
+    } else {
+      MLA_WAIT_VM(0);
+    }
     MLA_WAIT_LGKM0();
     MLA_BARRIER();
     return fsrc_next;
   };
   {
     const char* fsrc = tile_src(min(t0 + 3 * kTileTok, t_last));
-    for (int i = 0; i + 1 < n_tiles; ++i) fsrc = iteration(i, fsrc);
+    int i = 0;
+    for (; i + 3 < n_tiles; ++i) fsrc = iteration(i, fsrc, true, true);
+    if (i + 2 < n_tiles) iteration(i++, fsrc, false, true);
+    if (i + 1 < n_tiles) iteration(i, fsrc, false, false);
   }
-  // last tile: latent pass only
+  // last tile: latent pass only. The statistics are final (the last softmax
+  // ran in the previous iteration): 1/l of this wave's rows goes to the
+  // rescale slot of parity (i + 1) & 1, which no wave reads again, and the
+  // barrier after the latent pass publishes it
+  float* stat = (float*)(smem + kOffAlpha + (n_tiles & 1) * kRowsPerWg * 4);
   {
     const int i = n_tiles - 1;
     const int4 fl = *(const int4*)(smem + kOffFlag + (i & 1) * kWaves * 4);
+    if (half == 0) stat[rr] = l > 0.f ? 1.f / l : 0.f;
+    {
+      // lse = m + log2 l per score row, -inf when the row saw no position
+      const size_t rows_per_chunk = (size_t)p.q_tokens * kHeads;
+      const size_t row0 = (size_t)wi.slot * rows_per_chunk + qi * kHeads + hg * 32;
+      if (half == 0) p.part_lse[row0 + l32] = l > 0.f ? m + __log2f(l) : -INFINITY;
+    }
     if (fl.x | fl.y | fl.z | fl.w) rescale_o(i & 1, fl);
     const char* cur = kvb(i);
     const char* pbuf = smem + kOffP + (i & 1) * kPBytes;
@@ -700,18 +736,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     pv_step(cur, pbuf, 1);
   }
 
-  // the epilogue reuses both rings: no fetch may still be landing, and every
-  // wave must be past its last read
+  // the epilogue reuses the c_KV ring: no fetch may still be landing, and
+  // every wave must be past its last read (and its 1/l written)
   MLA_WAIT_VM(0);
-  MLA_WAIT_LGKM0();
-  MLA_BARRIER();
-  if (half == 0) ((float*)(smem + kOffStat))[rr] = l > 0.f ? 1.f / l : 0.f;
-  {
-    // lse = m + log2 l per score row, -inf when the row saw no position
-    const size_t rows_per_chunk = (size_t)p.q_tokens * kHeads;
-    const size_t row0 = (size_t)wi.slot * rows_per_chunk + qi * kHeads + hg * 32;
-    if (half == 0) p.part_lse[row0 + l32] = l > 0.f ? m + __log2f(l) : -INFINITY;
-  }
   MLA_WAIT_LGKM0();
   MLA_BARRIER();
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -723,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // after the last barrier): 8-byte units of 4 columns, unit ^ 2 (row % 16).
   float inv_l[4];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) inv_l[h] = ((const float*)(smem + kOffStat))[32 * h + l32];
+  for (int h = 0; h < 4; ++h) inv_l[h] = stat[32 * h + l32];
   char* tw = smem + w * (kRowsPerWg * kColsPerWave * 2);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
