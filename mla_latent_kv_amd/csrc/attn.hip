@@ -521,6 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // the softmax's ~90) is spread at most ~4 per slot.
   // kFetch: tile i + 3 exists; kConv: tile i + 2 exists. Every call passes
   // constants, so each inlined copy keeps only its own work.
+  f16x8 sa_pre[2];
   auto iteration = [&](int i, const char* fsrc, const bool kFetch, const bool kConv)
                        __attribute__((always_inline)) -> const char* {
     const int ts = t0 + i * kTileTok;
@@ -533,6 +534,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     char* cbuf = kvb(i + 2);
     // the rescale flags of tile i, read now and tested before its latent
     // MFMAs (phase B), so the read's latency hides behind the score chain
+    // the rescale flags of tile i, read now and tested before its latent
+    // MFMAs (phase B), so the read's latency hides behind the score chain;
+    // the first two score operands of tile i + 1 were read by the previous
+    // iteration (or before the loop) right after its barrier, under its last
+    // latent MFMAs
     const int4 flags = *(const int4*)(smem + kOffFlag + (i & 1) * kWaves * 4);
 
     // in-place bf16 -> fp16 of granule g (rows 4 g + w) of tile i + 2, read 4
@@ -585,8 +591,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
                      : lds_read16<f16x8>(kr1, r_off[ks - 32]);
     };
     f16x8 sa[4];
+    sa[0] = sa_pre[0];
+    sa[1] = sa_pre[1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sa[j] = s_frag(j);
+    for (int j = 2; j < 4; ++j) sa[j] = s_frag(j);
     MLA_SLOT();
     f32x16 s;
     u32x4 cv[2];
@@ -695,20 +703,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
       if (k >= 1 && k <= 27) stage(k - 1);
       // the next iteration's fetch source (scalar work, off the first slot)
       if (kFetch && k == 29) fsrc_next = tile_src(min(ts + 4 * kTileTok, t_last));
+      if (k == 28) {
+        // The barrier goes here, three MFMAs before the end: P, the rescale
+        // flags (stages 25-26) and the converted tile i + 2 are written, every
+        // operand read of tile i has been issued (the last at slot 25) and
+        // is waited for, so tile i's buffer is free for the next fetch; the
+        // last three MFMAs need registers only.
+        // Tile i + 2's k_R fetch has landed too (its nine fetches are all in).
+        if (kFetch) {
+          MLA_WAIT_VM(9);
+        } else {
+          MLA_WAIT_VM(0);
+        }
+        MLA_WAIT_LGKM0();
+        MLA_BARRIER();
+      }
+      // the next iteration's first score operands (tile i + 2, published by
+      // the barrier) under the last MFMAs
+      if (kConv && k == 29) sa_pre[0] = lds_read16<f16x8>(kvb(i + 2), s_at(0));
+      if (kConv && k == 30) sa_pre[1] = lds_read16<f16x8>(kvb(i + 2), s_at(1));
       MLA_SLOT();
     }
-    // tile i + 2's k_R fetch has landed too (its nine fetches are all in)
-    if (kFetch) {
-      MLA_WAIT_VM(9);
-    } else {
-      MLA_WAIT_VM(0);
-    }
-    MLA_WAIT_LGKM0();
-    MLA_BARRIER();
     return fsrc_next;
   };
   {
     const char* fsrc = tile_src(min(t0 + 3 * kTileTok, t_last));
+    sa_pre[0] = lds_read16<f16x8>(kvb(1), s_at(0));
+    sa_pre[1] = lds_read16<f16x8>(kvb(1), s_at(1));
     int i = 0;
     for (; i + 3 < n_tiles; ++i) fsrc = iteration(i, fsrc, true, true);
     if (i + 2 < n_tiles) iteration(i++, fsrc, false, true);
