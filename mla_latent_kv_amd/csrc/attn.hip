@@ -53,8 +53,9 @@
 //   tile i + 3 and the conversion of tile i + 2 beside it, then phase B, the
 //   latent MFMAs of tile i with the softmax of tile i + 1 cut into small
 //   stages between them. sched_barrier fixes each slot's contents so the
-//   operand reads stay ahead of their MFMAs. The barrier then publishes P and
-//   the converted tile for the next iteration.
+//   operand reads stay ahead of their MFMAs. The barrier, three MFMAs before
+//   the end of phase B, publishes P and the converted tile for the next
+//   iteration, whose first score operands are read under those last MFMAs.
 #include "common.h"
 
 namespace mla {

@@ -88,11 +88,15 @@ inline int default_split_target(int n_cu, int q_tokens) {
 inline Layout make_layout(int batch, int q_tokens, int max_seq_len, int split_target, bool one_round = false) {
   Layout L{};
   const int max_blocks = (max_seq_len + kBlock - 1) / kBlock;
-  // items: at most kPlanWaves * P on the searched plan, P + B on the simple
-  // one (sum_b ceil(L_b / C) <= total / C + B with C >= total / P); either way
-  // no more than one per cache block
+  // items: at most kPlanWaves * P on the searched plan (at most kPlanWaves
+  // rounds), P + B on the simple one (sum_b ceil(L_b / C) <= total / C + B
+  // with C >= total / P, i.e. at most 1 + ceil(B / P) rounds); either way no
+  // more than one per cache block
   L.positions = (split_target + 7) / 8 * 8;
-  L.depth = one_round ? 1 : kPlanWaves + (batch + split_target - 1) / split_target;
+  {
+    const int simple_rounds = 1 + (batch + split_target - 1) / split_target;
+    L.depth = one_round ? 1 : (simple_rounds > kPlanWaves ? simple_rounds : kPlanWaves);
+  }
   long long cap = (long long)L.depth * split_target;
   long long by_len = (long long)batch * max_blocks;
   L.max_chunks = (int)(cap < by_len ? cap : by_len);

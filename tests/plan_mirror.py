@@ -12,7 +12,7 @@ def layout(B, sq, max_seq_len, P):
     """(positions, depth, partial-slot capacity) of the workspace."""
     max_blocks = -(-max_seq_len // 64)
     positions = -(-P // 8) * 8
-    depth = KW + -(-B // P)
+    depth = max(KW, 1 + -(-B // P))   # searched plan: <= KW rounds; simple plan: <= 1 + ceil(B / P)
     cap = depth * P
     max_chunks = max(1, min(cap, B * max_blocks))
     return positions, depth, max_chunks
