@@ -126,6 +126,15 @@ __device__ __forceinline__ Pair32 pair32(float x) {
   return Pair32{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
 }
 
+// The same fetch with the LDS address given as a wave-uniform base plus an
+// immediate, added straight into m0 (one scalar instruction per fetch).
+__device__ __forceinline__ void dma16i(unsigned lds_base, int imm, const char* base, unsigned voff) {
+  asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
+               :
+               : "s"(lds_base), "i"(imm), "v"(voff), "s"(base)
+               : "m0");
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read16(const char* base, int off) {
   return __builtin_bit_cast(T, *(const u32x4*)(base + off));
@@ -201,10 +210,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // 8 w .. 8 w + 7 (128 B rows of 8 granules, stored at g ^ ((r / 2) % 8)):
   // lane holds row 8 w + lane / 8, slot lane % 8, logical granule
   // (lane % 8) ^ ((4 w + lane / 16) % 8).
+  // The row of fetch j is folded into the lane offset: fetch j reads
+  // src + 16 rows * (j / 4) + voff_row[j % 4] (the granule permutation
+  // repeats with period 4 in j), so a full tile's fetch needs no scalar
+  // address arithmetic.
   const unsigned voff_base = 16u * (unsigned)(lane ^ (2 * w));
-  auto voff_kv = [&](int j) { return voff_base ^ (16u * (j & 1)) ^ (128u * ((j >> 1) & 1)); };
-  const unsigned voff_kr =
-      (unsigned)((lane >> 3) * kRowBytes + kDLat * 2 + 16 * ((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)));
+  unsigned voff_row[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    voff_row[jj] = (voff_base ^ (16u * (jj & 1)) ^ (128u * ((jj >> 1) & 1))) + (unsigned)((4 * jj + w) * kRowBytes);
+  const unsigned voff_kr = (unsigned)((8 * w + (lane >> 3)) * kRowBytes + kDLat * 2 +
+                                      16 * ((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)));
   // block ids of this split, 64 per window: lane i holds the id of block
   // blk_base + i; a tile reads its id with one lane read
   const int32_t* btab = p.block_table + (size_t)b * p.max_blocks_per_seq;
@@ -213,16 +229,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   int blk_base = blk_first;
   // issued before the query loads below, consumed from tile 3 on
   int blk_lane = blk_first + lane <= blk_last ? btab[blk_first + lane] : 0;
-  auto tile_src = [&](int ts) -> const char* {
-    const int bi = ts / kBlock;
+  const int blk_max = (int)min(p.num_blocks - 1, (long long)0x7fffffff);
+  auto tile_src = [&](int ts) -> const char* {   // ts >= 0
+    const int bi = (int)((unsigned)ts / kBlock);
     if (bi >= blk_base + 64) {   // next window (splits longer than 4096 tokens)
       blk_base += 64;
       blk_lane = blk_base + lane <= blk_last ? btab[blk_base + lane] : 0;
       asm volatile("" : "+v"(blk_lane));
     }
-    long long blk = __builtin_amdgcn_readlane(blk_lane, bi - blk_base);
-    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);   // memory safety
-    return (const char*)p.cache + ((size_t)blk * kBlock + (ts % kBlock)) * kRowBytes;
+    const int blk = min(max(__builtin_amdgcn_readlane(blk_lane, bi - blk_base), 0), blk_max);   // memory safety
+    return (const char*)p.cache + (size_t)(unsigned)blk * (kBlock * kRowBytes) +
+           ((unsigned)ts % kBlock) * kRowBytes;
   };
   // c_KV fetch j of a tile with `valid` rows inside the split: rows at or past
   // it re-read the last valid row, so they hold finite values that the zero
@@ -230,11 +247,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // wave-uniform (scalar address arithmetic)
   auto fetch_kv = [&](const char* src, int i, int j, int valid) {
     const int srow = min(4 * j + w, valid - 1);
-    dma16(kvb(i) + 1024 * (4 * j + w), src + srow * kRowBytes, voff_kv(j));
+    dma16(kvb(i) + 1024 * (4 * j + w), src + (srow - 4 * (j & 3) - w) * kRowBytes, voff_row[j & 3]);
   };
-  auto fetch_kr = [&](const char* src, int i) {
-    dma16(krb(i) + 1024 * w, src + 8 * w * kRowBytes, voff_kr);
-  };
+  auto fetch_kr = [&](const char* src, int i) { dma16(krb(i) + 1024 * w, src, voff_kr); };
   // in-place bf16 -> fp16 of the c_KV granules this lane fetched (rows 4 j + w);
   // all reads first, then the conversions and writes
   auto convert_tile = [&](char* tb) {
@@ -506,10 +521,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
 
   // ---- main loop: iteration i = latent pass of tile i, scores and softmax of
   // tile i + 1, conversion of tile i + 2, fetch of tile i + 3. The body is one
-  // straight-line MFMA stream, compiled three ways: with the fetch and the
-  // conversion, with the conversion only (i = n - 3: tile i + 3 does not
-  // exist) and with neither (i = n - 2), so the last iterations do no dead
-  // work; all fetches are drained before the epilogue.
+  // straight-line MFMA stream, compiled four ways: with the fetch of a full
+  // tile and the conversion (three instructions per fetch: the row is in the
+  // lane offset), with the fetch of the split's last tile (rows past the
+  // split clamped to its last row) and the conversion (i = n - 4), with the
+  // conversion only (i = n - 3: tile i + 3 does not exist) and with neither
+  // (i = n - 2), so the last iterations do no dead work; all fetches are
+  // drained before the epilogue.
   const int t_last = t0 + (n_tiles - 1) * kTileTok;
   // One issue slot = one MFMA plus the loads, stores and VALU work placed
   // beside it; sched_barrier keeps every slot's work where it is written, so
@@ -520,10 +538,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
   // same wave (measured on gfx950: 8 VALU per MFMA take 42-47 cycles instead of
   // 32), so the VALU work of an iteration (the conversion's 96 instructions,
   // the softmax's ~90) is spread at most ~4 per slot.
-  // kFetch: tile i + 3 exists; kConv: tile i + 2 exists. Every call passes
-  // constants, so each inlined copy keeps only its own work.
+  // kFetch: tile i + 3 exists; kFull: it is not the split's last tile, so all
+  // its 32 rows lie inside the split and need no clamp; kConv: tile i + 2
+  // exists. Every call passes constants, so each inlined copy keeps only its
+  // own work.
   f16x8 sa_pre[2];
-  auto iteration = [&](int i, const char* fsrc, const bool kFetch, const bool kConv)
+  auto iteration = [&](int i, const char* fsrc, const bool kFetch, const bool kFull, const bool kConv)
                        __attribute__((always_inline)) -> const char* {
     const int ts = t0 + i * kTileTok;
     const char* cur = kvb(i);
@@ -533,8 +553,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     const int fts = min(ts + 3 * kTileTok, t_last);
     const int fvalid = wi.t_end - fts;
     char* cbuf = kvb(i + 2);
-    // the rescale flags of tile i, read now and tested before its latent
-    // MFMAs (phase B), so the read's latency hides behind the score chain
+    // LDS address of this wave's first c_KV row of tile i + 3
+    const unsigned f_lds = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)(kvb(i + 3) + 1024 * w);
     // the rescale flags of tile i, read now and tested before its latent
     // MFMAs (phase B), so the read's latency hides behind the score chain;
     // the first two score operands of tile i + 1 were read by the previous
@@ -611,7 +631,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
         S_MFMA_BF16(s, __builtin_bit_cast(bf16x8, sa[ks & 3]), qp[ks - 32]);
       }
       if (ks + 4 < 36) sa[ks & 3] = s_frag(ks + 4);
-      if (kFetch && ks < 8) fetch_kv(fsrc, i + 3, ks, fvalid);
+      if (kFetch && !kFull && ks < 8) fetch_kv(fsrc, i + 3, ks, fvalid);
+      if (kFetch && kFull && ks < 8)
+        dma16i(f_lds, 4096 * ks, ks < 4 ? fsrc : fsrc + 16 * kRowBytes, voff_row[ks & 3]);
       if (kFetch && ks == 8) fetch_kr(fsrc, i + 3);
       if (kConv && ks < 32 && (ks & 3) == 0) cv[(ks >> 2) & 1] = conv_read(ks >> 2);
       if (kConv && ks >= 4) {
@@ -732,9 +754,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     sa_pre[0] = lds_read16<f16x8>(kvb(1), s_at(0));
     sa_pre[1] = lds_read16<f16x8>(kvb(1), s_at(1));
     int i = 0;
-    for (; i + 3 < n_tiles; ++i) fsrc = iteration(i, fsrc, true, true);
-    if (i + 2 < n_tiles) iteration(i++, fsrc, false, true);
-    if (i + 1 < n_tiles) iteration(i, fsrc, false, false);
+    for (; i + 4 < n_tiles; ++i) fsrc = iteration(i, fsrc, true, true, true);
+    if (i + 3 < n_tiles) fsrc = iteration(i++, fsrc, true, false, true);
+    if (i + 2 < n_tiles) iteration(i++, fsrc, false, false, true);
+    if (i + 1 < n_tiles) iteration(i, fsrc, false, false, false);
   }
   // last tile: latent pass only. The statistics are final (the last softmax
   // ran in the previous iteration): 1/l of this wave's rows goes to the
