@@ -135,6 +135,21 @@ __device__ __forceinline__ void dma16i(unsigned lds_base, int imm, const char* b
                : "m0");
 }
 
+// max of three / two scores in one instruction each. fmaxf on values the
+// compiler cannot prove canonical (MFMA results from inline asm) costs an
+// extra canonicalizing instruction per operand; the scores are never
+// signalling NaNs, so the plain instructions give the same maxima.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read16(const char* base, int off) {
   return __builtin_bit_cast(T, *(const u32x4*)(base + off));
@@ -652,14 +667,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
     // about four VALU instructions, one per slot
     const int sts = ts + kTileTok;
     const int par1 = (i + 1) & 1;
-    float mx[4], mt = 0.f, alpha = 1.f, neg_m = 0.f, rsum[2] = {0.f, 0.f};
+    float mx[5], mt = 0.f, alpha = 1.f, neg_m = 0.f, rsum[2] = {0.f, 0.f};
     bool grow = false, rescale = false;
     int any_rescale = 0;
     f16x4 pq[4];
     // tokens of this lane's k-half below lim; a full tile needs no mask
     const int nv = lim - sts - 4 * half;
     const bool full = sts + kTileTok <= lim;   // wave-uniform
-    auto mx4 = [&](int q) { mx[q] = fmaxf(fmaxf(s[4 * q], s[4 * q + 1]), fmaxf(s[4 * q + 2], s[4 * q + 3])); };
+    // the tile's 16 scores of this lane: five max3 of 15 scores, then the
+    // five partial maxima and the 16th score
+    auto mx3 = [&](int q) { mx[q] = max3f(s[3 * q], s[3 * q + 1], s[3 * q + 2]); };
     auto stage = [&](int k) {
       if (k == 0) {
         // the chain's last MFMA (inline asm: the compiler does not count its
@@ -670,16 +687,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs p) {
           for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3)) < nv ? s[e] : -INFINITY;
         }
       } else if (k == 1) {
-        mx4(0);
-        mx4(1);
+        mx3(0);
+        mx3(1);
+        mx3(2);
       } else if (k == 2) {
-        mx4(2);
-        mx4(3);
+        mx3(3);
+        mx3(4);
       } else if (k == 3) {
-        mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+        mt = max2f(max3f(mx[0], mx[1], mx[2]), max3f(mx[3], mx[4], s[15]));
       } else if (k == 4) {
         const Pair32 pm = pair32(mt);
-        mt = fmaxf(pm.a, pm.b) * scale_log2;
+        mt = max2f(pm.a, pm.b) * scale_log2;
       } else if (k == 5) {
         grow = mt > m + kRescaleLog2;
         rescale = grow && m != -INFINITY;
