@@ -13,7 +13,11 @@ wait states the compiler itself emits for builtin MFMAs on gfx950:
   R2  the result registers of an MFMA are not read or written by another
       instruction (VALU, LDS, memory, an MFMA's A or B operand), where one of
       the two is asm, within 12 wait states of a 32x32 MFMA (8 passes) or 8 of
-      a 16x16 one (4 passes).
+      a 16x16 one (4 passes);
+  R3  the result of a transcendental VALU instruction (exp, log, rcp, rsq,
+      sqrt, sin, cos) is not read by an inline-asm instruction before one
+      wait state has passed (gfx950 needs one before any VALU consumer; the
+      compiler inserts it only in front of its own instructions).
 Wait states: one per instruction in between, n + 1 for `s_nop n`. An MFMA
 taking the previous one's result as its accumulator is forwarded by the
 hardware and exempt. The scan follows the text of the assembly (a straight-line
@@ -84,11 +88,19 @@ def _is_valu(op):
     return op.startswith("v_") and not _is_mfma(op)
 
 
+_TRANS = re.compile(r"^v_(exp|log|rcp|rcp_iflag|rsq|sqrt|sin|cos)_(f32|f16)")
+
+
 def scan(text):
     """List of hazard descriptions for the device assembly `text`."""
     ins = _instructions(text)
     found = []
     for k, (op, ops, line, asm) in enumerate(ins):
+        # R3: a transcendental's result read by the next instruction, in asm
+        if _TRANS.match(op) and ops and k + 1 < len(ins):
+            nop_, nops, nline, nasm = ins[k + 1]
+            if nasm and _is_valu(nop_) and any(_regs(o) & _regs(ops[0]) for o in nops[1:]):
+                found.append(f"R3: '{line}' then '{nline}' after 0 wait states")
         if not _is_mfma(op) or len(ops) < 4:
             continue
         dst = _regs(ops[0])
@@ -177,6 +189,17 @@ def test_scan_finds_planted_hazards():
         s_endpgm
     """
     assert any(h.startswith("R2") for h in scan(late))
+    # a transcendental's result read at once by an asm conversion (wrong
+    # values on the GPU); one instruction in between is enough
+    trans = """
+        v_exp_f32_e32 v9, v9
+        ;;#ASMSTART
+        v_cvt_pk_f16_f32 v6, v6, v9
+        ;;#ASMEND
+        s_endpgm
+    """
+    assert any(h.startswith("R3") for h in scan(trans))
+    assert scan(trans.replace(";;#ASMSTART", "s_nop 0\n        ;;#ASMSTART")) == []
 
 
 @pytest.mark.parametrize("src", ["attn.hip", "prep.hip", "merge.hip", "naive.hip"])
