@@ -48,9 +48,9 @@ QPROJ_WEIGHT_BYTES = (1536 * 7168 + 128 * 192 * 1536) * 2   # W_DQ and W_UQ, bf1
 # The figures belong to the workload and the attention source they were taken
 # on: for another workload, or when the source hash differs, traffic is null.
 ATTN_TRAFFIC = {"workload": "uniform_b32_l4096",
-                "src_sha256": "ffc945907ddf047e2f70aba3bae3b823648f60a0b466d848975eccd2c1375922",
-                "fetch_kib": 76289.7, "write_kib": 32896.0,
-                "fetch_scale": 1048576.0 / 524302.8, "write_scale": 1.0}
+                "src_sha256": "4194bb4f4ec7237603627b66cdc975c9efcc654655d82559428a1054a986d0a6",
+                "fetch_kib": 76340.2, "write_kib": 32896.0,
+                "fetch_scale": 1048576.0 / 524302.6, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("mla_latent_kv_amd/csrc/attn.hip", "mla_latent_kv_amd/csrc/common.h")
 
 
