@@ -1,5 +1,5 @@
 """Host mirror of the split plan that the decode's prep kernel computes on the
-GPU (csrc/prep.hip, plan_block), step for step, and of the workspace layout
+GPU (csrc/plan.h, plan_block), step for step, and of the workspace layout
 it is written into (csrc/common.h, make_layout). Host logic for the tests: the
 CPU test checks the plan's invariants on random batches, the GPU test checks
 that the device writes exactly this plan. Not part of the oracle: the plan

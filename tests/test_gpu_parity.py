@@ -20,6 +20,9 @@ SMALL = [
     synth.Spec("edges_sq1", 6, 1, (1, 31, 32, 33, 64, 65)),
     synth.Spec("edges_sq2", 5, 2, (2, 3, 32, 33, 129)),
     synth.Spec("qx3_b2", 2, 1, (700, 3000), q_scale=3.0),
+    # 128 and more query rows: the absorb runs its wide tile (4 heads x 64 columns)
+    synth.Spec("rows128_sq1", 128, 1, ("uniform", 1, 200)),
+    synth.Spec("rows160_sq2", 80, 2, ("uniform", 2, 150)),
 ]
 
 

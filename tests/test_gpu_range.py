@@ -66,6 +66,36 @@ def test_q_abs_past_the_scaled_range_is_flagged():
     assert flags == binding.MLA_RANGE_QABS
 
 
+def test_range_flags_rewritten_by_either_absorb_tile():
+    """Batches below 128 query rows run the narrow absorb tile, from 128 rows on
+    the wide one (half as many workgroups, each writing two flags): every call
+    rewrites every flag, so a flagged call followed by a clean one on the same
+    workspace reads clean, in either order."""
+    import torch
+    from mla_latent_kv_amd import binding, device
+    cases = {
+        "narrow_huge": synth.Spec("narrow_huge", 1, 1, (300,), q_scale=2.0 ** 24),
+        "wide_clean": synth.Spec("wide_clean", 128, 1, ("uniform", 1, 150)),
+        "wide_huge": synth.Spec("wide_huge", 128, 1, ("uniform", 1, 150), q_scale=2.0 ** 24),
+        "narrow_clean": synth.Spec("narrow_clean", 2, 1, (300, 64)),
+    }
+    dec = binding.MLADecoder(0, max_q_tokens=2, softmax_scale=1e-9)
+    batches = {k: synth.make_batch(v, seed=54 + i) for i, (k, v) in enumerate(cases.items())}
+    ws_bytes = max(dec.workspace_size(b["seq_lens"].shape[0], b["q_nope"].shape[1],
+                                      int(b["seq_lens"].max())) for b in batches.values())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    expect = {"narrow_huge": binding.MLA_RANGE_QABS, "wide_clean": 0,
+              "wide_huge": binding.MLA_RANGE_QABS, "narrow_clean": 0}
+    for name in ("narrow_huge", "wide_clean", "wide_huge", "narrow_clean"):
+        say(f"case {name}")
+        d = device.upload(batches[name])
+        dec(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"], d["block_table"],
+            d["seq_lens"], d["max_seq_len"], workspace=ws)
+        torch.cuda.synchronize()
+        assert binding.mla_decode_range_flags(dec.ctx, ws) == expect[name], name
+    dec.close()
+
+
 def test_c_kv_past_fp16_range_saturates():
     spec = synth.Spec("c_big", 2, 1, (200, 333))
     batch = synth.make_batch(spec, seed=53)

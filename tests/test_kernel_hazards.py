@@ -202,7 +202,7 @@ def test_scan_finds_planted_hazards():
     assert scan(trans.replace(";;#ASMSTART", "s_nop 0\n        ;;#ASMSTART")) == []
 
 
-@pytest.mark.parametrize("src", ["attn.hip", "prep.hip", "merge.hip", "naive.hip"])
+@pytest.mark.parametrize("src", ["attn.hip", "prep.hip", "prep_wide.hip", "merge.hip", "naive.hip"])
 def test_no_mfma_hazards(src, tmp_path):
     hz = scan(_device_asm(src, tmp_path))
     assert hz == [], "\n".join(hz[:20])
