@@ -26,7 +26,7 @@ Sources (the pages are web write-ups of the DeepSeek-V3 technical report):
   output side), section 2.3 (decoupled RoPE: q^R per head, k^R shared across
   heads).
 
-Readings where the pages are silent or garbled (each is repeated in the design doc):
+Readings where the pages are silent or garbled:
 
 * softmax scale: no page gives one; 1/sqrt(d_nope + d_rope) = 1/sqrt(192),
   the width of the per-head query/key each score is a dot product over.
