@@ -22,6 +22,7 @@ SMALL = [
     synth.Spec("qx3_b2", 2, 1, (700, 3000), q_scale=3.0),
     # 128 and more query rows: the absorb runs its wide tile (4 heads x 64 columns)
     synth.Spec("rows128_sq1", 128, 1, ("uniform", 1, 200)),
+    synth.Spec("rows129_sq1", 129, 1, ("uniform", 1, 100)),   # one row in the last 32-row tile
     synth.Spec("rows160_sq2", 80, 2, ("uniform", 2, 150)),
 ]
 
