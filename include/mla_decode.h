@@ -80,6 +80,9 @@ enum mla_decode_status {
   MLA_ERR_MISALIGNED = -3,      /* a pointer not 16-byte aligned */
   MLA_ERR_WORKSPACE = -4,       /* workspace null or smaller than required */
   MLA_ERR_HIP = -5,             /* a HIP runtime call or launch failed */
+  MLA_ERR_PRECONDITION = -6,    /* inputs break a documented precondition:
+                                   mla_decode_check_inputs, or any entry point
+                                   of the debug build (below) */
 };
 
 typedef struct mla_decode_config {
@@ -136,6 +139,42 @@ int mla_decode_workspace_size(const mla_decode_ctx* ctx, int32_t batch, int32_t 
  * and must not be shared by calls that may overlap. */
 int mla_decode_run(const mla_decode_ctx* ctx, const mla_decode_args* args, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* Host-side check of the preconditions on the decode inputs, on HOST copies
+ * of seq_lens (int32 [batch]) and block_table (int32 [batch,
+ * max_blocks_per_seq], row-major) with the same meaning as in
+ * mla_decode_args. The layout it checks is the paged cache above: token j of
+ * sequence b is row j % 64 of physical block block_table[b, j / 64]
+ * ("DeepSeek-V3" page at ailearn.mscapital.top, MLA section: each cached
+ * token is one 512 + 64 wide row). It requires, per sequence b:
+ *   - 0 <= L_b <= max_seq_len;
+ *   - block_table[b, k] in [0, num_blocks) for every block k < ceil(L_b / 64)
+ *     the sequence uses (entries past them are not read);
+ *   - the rows of its new tokens (positions max(0, L_b - q_tokens) .. L_b - 1)
+ *     in slots no other sequence's new tokens use. Older blocks may be shared
+ *     between sequences (a common prefix); a new token's row may not.
+ * Returns MLA_OK, MLA_ERR_PRECONDITION with *first_bad = the lowest-numbered
+ * sequence that breaks one (for a shared new-token slot: every sequence of
+ * the group but the lowest-numbered one), or MLA_ERR_INVALID_ARG (NULL
+ * arrays, batch outside 1..1000000, q_tokens < 1, max_blocks_per_seq < 1,
+ * max_seq_len outside 1..64 * max_blocks_per_seq, num_blocks < 1).
+ * *first_bad is -1 unless the status is MLA_ERR_PRECONDITION; first_bad may
+ * be NULL. Reads only seq_lens[0..batch) and, of row b, the entries the
+ * sequence uses. Pure host code: no GPU needed, no context, thread-safe.
+ *
+ * The release kernels never read outside the cache for any input (a block id
+ * out of range is clamped to [0, num_blocks), a length to [0, max_seq_len]);
+ * such inputs give unspecified results. The debug build (libmla_decode_debug.so:
+ * the same kernels, compiled with MLA_DEBUG_CHECKS) instead copies seq_lens
+ * and block_table to the host and runs this check at the start of
+ * mla_decode_run, mla_decode_run_profiled, mla_decode_run_noalloc,
+ * mla_cache_append and mla_naive_run (max_seq_len = 64 * max_blocks_per_seq
+ * for the append), returning MLA_ERR_PRECONDITION before any launch. Those
+ * calls then synchronise `stream` and allocate host memory, so the debug
+ * build is not for graph capture or tight loops. */
+int mla_decode_check_inputs(const int32_t* seq_lens, const int32_t* block_table, int32_t batch,
+                            int32_t q_tokens, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                            int64_t num_blocks, int32_t* first_bad);
 
 /* mla_decode_run, plus timing marks for measurement tools: records the
  * hipEvent_t handles events[0] and events[1] before the preparation launch

@@ -13,6 +13,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+# the same kernels with host-side precondition checks before every launch
+DEBUG_LIB_PATH = os.path.join(HERE, "libmla_decode_debug.so")
 
 MLA_OK = 0
 N_HEADS, D_NOPE, D_ROPE, D_LATENT, D_V, BLOCK = 128, 128, 64, 512, 128, 64
@@ -126,14 +128,15 @@ class MlaNaiveArgs(ctypes.Structure):
     ]
 
 
-_lib = None
+_libs = {}
+MLA_ERR_PRECONDITION = -6
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the built library (once). Raises RuntimeError when it is absent."""
-    global _lib
-    if _lib is not None:
-        return _lib
+    """Load a built library (once per path; the release build by default).
+    Raises RuntimeError when it is absent."""
+    if path in _libs:
+        return _libs[path]
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m mla_latent_kv_amd.build` "
@@ -194,8 +197,31 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_destroy.restype = None
     lib.mla_decode_status_string.argtypes = [ctypes.c_int]
     lib.mla_decode_status_string.restype = ctypes.c_char_p
-    _lib = lib
+    lib.mla_decode_check_inputs.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]
+    lib.mla_decode_check_inputs.restype = ctypes.c_int
+    _libs[path] = lib
     return lib
+
+
+def mla_decode_check_inputs(seq_lens, block_table, q_tokens: int, max_seq_len: int,
+                            num_blocks: int):
+    """The library's host-side precondition check on host arrays (numpy or CPU
+    tensors): seq_lens int32 [B], block_table int32 [B, max_blocks_per_seq].
+    Returns (status, first_bad): (0, -1) when the inputs meet the decode
+    preconditions, (MLA_ERR_PRECONDITION, b) naming the lowest-numbered
+    sequence that breaks one."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
+    table = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    if lens.ndim != 1 or table.ndim != 2 or table.shape[0] != lens.shape[0]:
+        raise ValueError("seq_lens must be [B] and block_table [B, max_blocks_per_seq]")
+    bad = ctypes.c_int32(-2)
+    st = load_library().mla_decode_check_inputs(
+        lens.ctypes.data, table.ctypes.data, int(lens.shape[0]), int(q_tokens), int(table.shape[1]),
+        int(max_seq_len), int(num_blocks), ctypes.byref(bad))
+    return int(st), int(bad.value)
 
 
 def mla_decode_status_string(status: int) -> str:

@@ -1,4 +1,7 @@
-"""Build libmla_decode.so (the HIP kernels and the C ABI) for gfx950 in-tree.
+"""Build libmla_decode.so (the HIP kernels and the C ABI) for gfx950 in-tree,
+and beside it libmla_decode_debug.so: the same objects except the C ABI,
+compiled with MLA_DEBUG_CHECKS (host-side precondition checks before every
+launch).
 
 Usage: python -m mla_latent_kv_amd.build   (or call build()).
 """
@@ -15,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.hip", "prep.hip", "prep_wide.hip", "attn.hip", "merge.hip", "wpack.hip", "append.hip", "oproj.hip", "qproj.hip", "naive.hip"]
+DEBUG_LIB = os.path.join(HERE, "libmla_decode_debug.so")
+SOURCES = ["api.hip", "check.cpp", "prep.hip", "prep_wide.hip", "attn.hip", "merge.hip", "wpack.hip", "append.hip", "oproj.hip", "qproj.hip", "naive.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -33,9 +37,11 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(src: str, debug: bool = False) -> str:
+    stem = os.path.splitext(src)[0] + ("_debug" if debug else "")
+    out = os.path.join(OBJ, stem + ".o")
+    defs = ["-DMLA_DEBUG_CHECKS"] if debug else []
+    cmd = [hipcc(), *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
@@ -46,19 +52,27 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("link of libmla_decode.so failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the release and debug libraries; returns
+    the release library's path."""
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = [(src, False) for src in SOURCES] + [("api.hip", True)]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    release = objs[:len(SOURCES)]
+    _link(release, LIB)
+    _link([objs[-1]] + release[1:], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEBUG_LIB}")
     return LIB
 
 

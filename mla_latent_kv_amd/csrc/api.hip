@@ -3,10 +3,12 @@
 // plan -> absorb -> attention -> merge (decode) and product -> finish (cache
 // append), all on the caller's stream.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/mla_decode.h"
 #include "common.h"
@@ -31,6 +33,41 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int32_t kMaxNaiveLen = 1 << 20;   // tokens per sequence on the naive path
 
+#ifdef MLA_DEBUG_CHECKS
+// Debug build: the preconditions of mla_decode_check_inputs on host copies of
+// the lengths and the block table, before any launch (synchronises `stream`).
+int debug_check(const int32_t* seq_lens, const int32_t* block_table, int batch, int q_tokens, int mbps,
+                int max_seq_len, int64_t num_blocks, hipStream_t stream) {
+  std::vector<int32_t> lens, table;
+  try {
+    lens.resize((size_t)batch);
+    table.resize((size_t)batch * (size_t)mbps);
+  } catch (const std::bad_alloc&) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (hipMemcpyAsync(lens.data(), seq_lens, lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(table.data(), block_table, table.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return mla_decode_check_inputs(lens.data(), table.data(), batch, q_tokens, mbps, max_seq_len, num_blocks,
+                                 nullptr);
+}
+#define MLA_DEBUG_CHECK(...)                              \
+  do {                                                    \
+    const int st_ = debug_check(__VA_ARGS__);             \
+    if (st_ != MLA_OK) {                                  \
+      if (prev != ctx->device) (void)hipSetDevice(prev);  \
+      return st_;                                         \
+    }                                                     \
+  } while (0)
+#else
+#define MLA_DEBUG_CHECK(...) \
+  do {                       \
+  } while (0)
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -43,6 +80,7 @@ const char* mla_decode_status_string(int status) {
     case MLA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_PRECONDITION: return "inputs break a documented precondition";
     default: return "unknown status";
   }
 }
@@ -113,6 +151,8 @@ int run_impl(const mla_decode_ctx* ctx, const mla_decode_args* a, void* workspac
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
   if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  MLA_DEBUG_CHECK(a->seq_lens, a->block_table, a->batch, a->q_tokens, a->max_blocks_per_seq, a->max_seq_len,
+                  a->num_blocks, stream);
 
   char* ws = (char*)workspace;
   mla::WorkItem* work = (mla::WorkItem*)(ws + L.work);
@@ -267,6 +307,9 @@ int mla_cache_append(const mla_decode_ctx* ctx, const mla_append_args* a, void* 
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
   if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  MLA_DEBUG_CHECK(a->seq_lens, a->block_table, a->batch, a->q_tokens, a->max_blocks_per_seq,
+                  (int)std::min<long long>((long long)mla::kBlock * a->max_blocks_per_seq, 0x7fffffff),
+                  a->num_blocks, stream);
   const double base = a->rope_base > 0.f ? (double)a->rope_base : 10000.0;
   const int status =
       mla::launch_append((const uint16_t*)a->hidden, (const uint16_t*)a->w_kv, (uint16_t*)a->kv_cache,
@@ -421,6 +464,8 @@ int mla_naive_run(const mla_decode_ctx* ctx, const mla_naive_args* a, void* work
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_HIP;
   if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return MLA_ERR_HIP;
+  MLA_DEBUG_CHECK(a->seq_lens, a->block_table, a->batch, a->q_tokens, a->max_blocks_per_seq, a->max_seq_len,
+                  a->num_blocks, stream);
   const int status =
       mla::launch_naive((const uint16_t*)a->q_nope, (const uint16_t*)a->q_pe, (const uint16_t*)a->w_uk,
                         (const uint16_t*)a->w_uv, (const uint16_t*)a->kv_cache, a->block_table, a->seq_lens, a->out,

@@ -90,20 +90,14 @@ def draw_lengths(spec: Spec, rng: np.random.Generator) -> np.ndarray:
     return lens
 
 
-def make_batch(spec: Spec, seed: int, poison: bool = True) -> dict:
-    """Draw one batch. Returns uint16 bf16-bit arrays and int32 tables:
-
-    q_nope [B, Sq, H, d_nope], q_pe [B, Sq, H, d_rope], w_uk [H, d_nope, d_latent],
-    w_uv [H, d_v, d_latent], cache [num_blocks, block, d_latent + d_rope],
-    block_table [B, max_blocks_per_seq] (unused tail entries -1),
-    seq_lens [B], plus the host-side ``max_seq_len``.
-
-    Cache row j of sequence b is [c_KV (d_latent) | k_R (d_rope)] in physical
-    block block_table[b, j // block], slot j % block. The unused slots of each
-    sequence's last block hold bf16 NaN when ``poison`` is set.
-    """
+def make_tables(spec: Spec, seed: int):
+    """The lengths and the block table of make_batch(spec, seed) alone (same
+    draws): (seq_lens [B], block_table [B, max_blocks_per_seq] with unused
+    tail entries -1, max_seq_len, total blocks). Each sequence owns
+    ceil(L_b / block) physical blocks, a random permutation of all blocks
+    when the spec is paged, in order otherwise."""
     ss = np.random.SeedSequence(seed).spawn(7)
-    r_len, r_perm, r_qn, r_qp, r_wk, r_wv, r_c = (np.random.default_rng(s) for s in ss)
+    r_len, r_perm = np.random.default_rng(ss[0]), np.random.default_rng(ss[1])
     lens = draw_lengths(spec, r_len)
     bs = spec.block_size
     nblk = (lens + bs - 1) // bs
@@ -120,6 +114,26 @@ def make_batch(spec: Spec, seed: int, poison: bool = True) -> dict:
     for b in range(spec.batch):
         table[b, :nblk[b]] = perm[off:off + nblk[b]]
         off += int(nblk[b])
+    return lens, table, max_seq, total_blocks
+
+
+def make_batch(spec: Spec, seed: int, poison: bool = True) -> dict:
+    """Draw one batch. Returns uint16 bf16-bit arrays and int32 tables:
+
+    q_nope [B, Sq, H, d_nope], q_pe [B, Sq, H, d_rope], w_uk [H, d_nope, d_latent],
+    w_uv [H, d_v, d_latent], cache [num_blocks, block, d_latent + d_rope],
+    block_table [B, max_blocks_per_seq] (unused tail entries -1),
+    seq_lens [B], plus the host-side ``max_seq_len``.
+
+    Cache row j of sequence b is [c_KV (d_latent) | k_R (d_rope)] in physical
+    block block_table[b, j // block], slot j % block. The unused slots of each
+    sequence's last block hold bf16 NaN when ``poison`` is set.
+    """
+    ss = np.random.SeedSequence(seed).spawn(7)
+    r_qn, r_qp, r_wk, r_wv, r_c = (np.random.default_rng(s) for s in ss[2:])
+    lens, table, max_seq, total_blocks = make_tables(spec, seed)
+    bs = spec.block_size
+    nblk = (lens + bs - 1) // bs
 
     B, Sq, H = spec.batch, spec.q_tokens, spec.n_heads
     q_nope = _normal_bits(r_qn, (B, Sq, H, spec.d_nope), spec.q_scale)

@@ -30,7 +30,8 @@ def test_every_declared_symbol_is_exported():
                         "mla_query_project_workspace_size", "mla_pack_weight",
                         "mla_naive_workspace_size", "mla_naive_run",
                         "mla_project_new_tokens_workspace_size", "mla_project_new_tokens",
-                        "mla_decode_range_flags", "mla_decode_run_noalloc"}
+                        "mla_decode_range_flags", "mla_decode_run_noalloc",
+                        "mla_decode_check_inputs"}
     lib = _lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -40,7 +41,7 @@ def test_status_strings():
     from mla_latent_kv_amd import binding
     _lib()
     assert binding.mla_decode_status_string(0) == "ok"
-    for code in (-1, -2, -3, -4, -5):
+    for code in (-1, -2, -3, -4, -5, -6):
         s = binding.mla_decode_status_string(code)
         assert s and s != "unknown status"
     assert binding.mla_decode_status_string(-99) == "unknown status"
