@@ -194,3 +194,36 @@ def test_one_item_longer_than_a_block_table_window(sq):
     got = run_gpu(batch, split_target=1)
     ref = oracle(batch, path="absorb")
     assert_parity(got, ref, spec.name)
+
+
+# batches past the searched plan's reach: the simple plan (every sequence cut
+# at one chunk length, full chunks first), and the largest searched sort
+# (the oracle's per-sequence cost makes every output of a thousand sequences
+# a minute of host time: 256 sampled (sequence, head) pairs each, every output
+# finite)
+LARGE_BATCH = [
+    synth.Spec("simple_b1100", 1100, 1, ("uniform", 1, 200)),
+    synth.Spec("sorted_b1024", 1024, 1, ("uniform", 1, 300)),
+    # 8192 sequences (8192 query rows for the absorb, 256 row tiles of the
+    # wide tile) and 4096 two-token sequences
+    synth.Spec("simple_b8192", 8192, 1, ("uniform", 1, 64)),
+    synth.Spec("simple_b4096_sq2", 4096, 2, ("uniform", 2, 64)),
+]
+
+
+@pytest.mark.parametrize("spec", LARGE_BATCH, ids=lambda s: s.name)
+def test_large_batches(spec, n_sample=256):
+    from tests import plan_mirror as pm
+    import torch
+    batch = synth.make_batch(spec, seed=43)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    P = n_cu if spec.q_tokens == 1 else n_cu // 2
+    r = pm.check(batch["seq_lens"], int(batch["max_seq_len"]), P)
+    say(f"case {spec.name}: B={spec.batch} Sq={spec.q_tokens} tokens={int(batch['seq_lens'].sum())} "
+        f"search={r['search']} items={r['n_items']}")
+    got = run_gpu(batch)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(44)
+    bs = rng.choice(spec.batch, n_sample, replace=False)
+    sample = [(int(b), int(rng.integers(0, 128))) for b in bs]
+    assert_parity(got, oracle(batch, sample=sample), f"{spec.name} {n_sample} sampled (b, h)")
