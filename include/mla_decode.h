@@ -149,15 +149,16 @@ int mla_decode_run(const mla_decode_ctx* ctx, const mla_decode_args* args, void*
  * token is one 512 + 64 wide row). It requires, per sequence b:
  *   - 0 <= L_b <= max_seq_len;
  *   - block_table[b, k] in [0, num_blocks) for every block k < ceil(L_b / 64)
- *     the sequence uses (entries past them are not read);
+ *     the sequence uses (entries past them are not read), no two of them equal;
  *   - the rows of its new tokens (positions max(0, L_b - q_tokens) .. L_b - 1)
- *     in slots no other sequence's new tokens use. Older blocks may be shared
+ *     in slots no other sequence's new tokens use. Blocks may be shared
  *     between sequences (a common prefix); a new token's row may not.
  * Returns MLA_OK, MLA_ERR_PRECONDITION with *first_bad = the lowest-numbered
  * sequence that breaks one (for a shared new-token slot: every sequence of
  * the group but the lowest-numbered one), or MLA_ERR_INVALID_ARG (NULL
  * arrays, batch outside 1..1000000, q_tokens < 1, max_blocks_per_seq < 1,
- * max_seq_len outside 1..64 * max_blocks_per_seq, num_blocks < 1).
+ * max_seq_len outside 1..64 * max_blocks_per_seq, num_blocks < 1, or host
+ * memory too short for the check's lists of blocks and slots).
  * *first_bad is -1 unless the status is MLA_ERR_PRECONDITION; first_bad may
  * be NULL. Reads only seq_lens[0..batch) and, of row b, the entries the
  * sequence uses. Pure host code: no GPU needed, no context, thread-safe.

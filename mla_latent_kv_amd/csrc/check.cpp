@@ -22,10 +22,12 @@ namespace {
 constexpr int32_t kBlockTokens = 64;
 constexpr int32_t kMaxBatchRows = 1000000;
 
-struct Slot {
-  int64_t key;   // physical block * 64 + slot
+struct Use {
+  int64_t key;   // a physical block, or a physical block * 64 + slot
   int32_t seq;
 };
+
+bool by_key_then_seq(const Use& x, const Use& y) { return x.key != y.key ? x.key < y.key : x.seq < y.seq; }
 
 }  // namespace
 
@@ -39,45 +41,59 @@ extern "C" int mla_decode_check_inputs(const int32_t* seq_lens, const int32_t* b
     return MLA_ERR_INVALID_ARG;
 
   int32_t bad = batch;   // lowest violating sequence so far (batch = none)
-  std::vector<Slot> slots;
+  // pass 1: lengths and block ranges; count what pass 2 collects
+  std::vector<char> ok((size_t)batch, 1);
+  size_t n_blocks = 0, n_slots = 0;
   try {
-    slots.reserve((size_t)batch * (size_t)std::min(q_tokens, max_seq_len));
-  } catch (const std::bad_alloc&) {
-    return MLA_ERR_INVALID_ARG;
-  }
-  for (int32_t b = 0; b < batch; ++b) {
-    const int32_t len = seq_lens[b];
-    // 0 <= L_b <= max_seq_len; this also keeps every table read below inside
-    // row b, since max_seq_len <= 64 * max_blocks_per_seq
-    if (len < 0 || len > max_seq_len) {
-      bad = std::min(bad, b);
-      continue;
-    }
-    const int32_t* row = block_table + (int64_t)b * max_blocks_per_seq;
-    const int32_t used = (len + kBlockTokens - 1) / kBlockTokens;
-    bool ok = true;
-    for (int32_t k = 0; k < used; ++k)
-      if (row[k] < 0 || (int64_t)row[k] >= num_blocks) {
-        ok = false;
-        break;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t len = seq_lens[b];
+      // 0 <= L_b <= max_seq_len; this also keeps every table read below inside
+      // row b, since max_seq_len <= 64 * max_blocks_per_seq
+      if (len < 0 || len > max_seq_len) {
+        ok[b] = 0;
+        bad = std::min(bad, b);
+        continue;
       }
-    if (!ok) {
-      bad = std::min(bad, b);
-      continue;
+      const int32_t* row = block_table + (int64_t)b * max_blocks_per_seq;
+      const int32_t used = (len + kBlockTokens - 1) / kBlockTokens;
+      for (int32_t k = 0; k < used && ok[b]; ++k)
+        if (row[k] < 0 || (int64_t)row[k] >= num_blocks) ok[b] = 0;
+      if (!ok[b]) {
+        bad = std::min(bad, b);
+        continue;
+      }
+      n_blocks += (size_t)used;
+      n_slots += (size_t)std::min(len, q_tokens);
     }
-    // the slots of the new tokens, positions max(0, L_b - Sq) .. L_b - 1
-    for (int32_t j = std::max(0, len - q_tokens); j < len; ++j)
-      slots.push_back(Slot{(int64_t)row[j / kBlockTokens] * kBlockTokens + j % kBlockTokens, b});
+    // pass 2: the blocks each sequence uses, and its new tokens' slots
+    // (positions max(0, L_b - Sq) .. L_b - 1)
+    std::vector<Use> blocks, slots;
+    blocks.reserve(n_blocks);
+    slots.reserve(n_slots);
+    for (int32_t b = 0; b < batch; ++b) {
+      if (!ok[b]) continue;
+      const int32_t len = seq_lens[b];
+      const int32_t* row = block_table + (int64_t)b * max_blocks_per_seq;
+      for (int32_t k = 0; k < (len + kBlockTokens - 1) / kBlockTokens; ++k) blocks.push_back(Use{row[k], b});
+      for (int32_t j = std::max(0, len - q_tokens); j < len; ++j)
+        slots.push_back(Use{(int64_t)row[j / kBlockTokens] * kBlockTokens + j % kBlockTokens, b});
+    }
+    // a sequence maps two of its own blocks to one physical block: its
+    // history would repeat rows (blocks of different sequences may coincide,
+    // as a shared prefix would)
+    std::sort(blocks.begin(), blocks.end(), by_key_then_seq);
+    for (size_t i = 1; i < blocks.size(); ++i)
+      if (blocks[i].key == blocks[i - 1].key && blocks[i].seq == blocks[i - 1].seq)
+        bad = std::min(bad, blocks[i].seq);
+    // two sequences' new tokens stored in one slot: every sequence of such a
+    // group but the lowest-numbered one breaks the layout
+    std::sort(slots.begin(), slots.end(), by_key_then_seq);
+    for (size_t i = 1; i < slots.size(); ++i)
+      if (slots[i].key == slots[i - 1].key && slots[i].seq != slots[i - 1].seq)
+        bad = std::min(bad, slots[i].seq);
+  } catch (const std::bad_alloc&) {
+    return MLA_ERR_INVALID_ARG;   // the host cannot hold the check's lists
   }
-  // two new tokens stored in one slot: every sequence of such a group but
-  // the lowest-numbered one violates the layout (the older prefix blocks may
-  // be shared; a new token's row may not)
-  std::sort(slots.begin(), slots.end(), [](const Slot& x, const Slot& y) {
-    return x.key != y.key ? x.key < y.key : x.seq < y.seq;
-  });
-  for (size_t i = 1; i < slots.size(); ++i)
-    if (slots[i].key == slots[i - 1].key && slots[i].seq != slots[i - 1].seq)
-      bad = std::min(bad, slots[i].seq);
   if (bad == batch) return MLA_OK;
   if (first_bad) *first_bad = bad;
   return MLA_ERR_PRECONDITION;

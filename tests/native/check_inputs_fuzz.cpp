@@ -29,18 +29,35 @@ int expected(const int32_t* lens, const int32_t* table, int batch, int sq, int m
     for (int k = 0; k < (lens[b] + 63) / 64; ++k)
       if (table[(int64_t)b * mbps + k] < 0 || table[(int64_t)b * mbps + k] >= nblk) ok[b] = 0;
   }
-  auto slot = [&](int b, int j) { return (int64_t)table[(int64_t)b * mbps + j / 64] * 64 + j % 64; };
+  // the blocks of one sequence are distinct
   for (int b = 0; b < batch; ++b) {
     if (!ok[b]) continue;
-    for (int a = 0; a < b && ok[b]; ++a) {
-      if (!ok[a]) continue;
+    const int used = (lens[b] + 63) / 64;
+    for (int k = 0; k < used; ++k)
+      for (int k2 = k + 1; k2 < used; ++k2)
+        if (table[(int64_t)b * mbps + k] == table[(int64_t)b * mbps + k2]) ok[b] = 0;
+  }
+  std::vector<char> clash(batch, 0);
+  auto slot = [&](int b, int j) { return (int64_t)table[(int64_t)b * mbps + j / 64] * 64 + j % 64; };
+  // a new-token slot already used by a lower-numbered sequence whose lengths
+  // and block ids are in range (its own block repeats do not exempt it)
+  auto in_range = [&](int a) {
+    if (lens[a] < 0 || lens[a] > max_len) return false;
+    for (int k = 0; k < (lens[a] + 63) / 64; ++k)
+      if (table[(int64_t)a * mbps + k] < 0 || table[(int64_t)a * mbps + k] >= nblk) return false;
+    return true;
+  };
+  for (int b = 0; b < batch; ++b) {
+    if (!in_range(b)) continue;
+    for (int a = 0; a < b && !clash[b]; ++a) {
+      if (!in_range(a)) continue;
       for (int j = lens[b] - sq > 0 ? lens[b] - sq : 0; j < lens[b]; ++j)
         for (int i = lens[a] - sq > 0 ? lens[a] - sq : 0; i < lens[a]; ++i)
-          if (slot(b, j) == slot(a, i)) ok[b] = 0;
+          if (slot(b, j) == slot(a, i)) clash[b] = 1;
     }
   }
   for (int b = 0; b < batch; ++b)
-    if (!ok[b]) {
+    if (!ok[b] || clash[b]) {
       *bad = b;
       return MLA_ERR_PRECONDITION;
     }

@@ -109,6 +109,18 @@ def test_shared_prefix_blocks_are_allowed():
     assert check(np.array([40, 40], np.int32), table, 1, 128, 3) == (PRE, 1)
 
 
+def test_a_sequence_repeating_one_of_its_blocks():
+    # sequence 0 maps its first and third logical blocks to physical block 3
+    lens, table = _base()
+    t = table.copy()
+    t[0, 2] = 3
+    assert check(lens, t, 1, 192, 5) == (PRE, 0)
+    # a repeat past the blocks the sequence uses is never read
+    t = table.copy()
+    t[1, 1] = 1
+    assert check(lens, t, 1, 192, 5) == (0, -1)
+
+
 def test_lowest_offender_is_reported():
     lens = np.array([10, 900, 10, -5], np.int32)
     table = np.array([[0, 9], [1, 9], [2, 9], [3, 9]], np.int32)
@@ -135,12 +147,14 @@ def test_random_cases_match_a_restatement():
     rng = np.random.default_rng(3)
 
     def want(lens, table, sq, max_len, nblk):
-        ok = []
+        in_range, ok = [], []
         for b, L in enumerate(lens):
-            ok.append(0 <= L <= max_len and all(0 <= table[b, k] < nblk for k in range(-(-L // 64))))
+            used = [int(table[b, k]) for k in range(-(-L // 64))] if 0 <= L <= max_len else None
+            in_range.append(used is not None and all(0 <= x < nblk for x in used))
+            ok.append(in_range[b] and len(set(used)) == len(used))
         seen = {}
         for b, L in enumerate(lens):
-            if not ok[b]:
+            if not in_range[b]:
                 continue
             slots = {int(table[b, j // 64]) * 64 + j % 64 for j in range(max(0, L - sq), L)}
             if any(s in seen for s in slots):
