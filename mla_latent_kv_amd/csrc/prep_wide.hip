@@ -25,6 +25,18 @@ constexpr int kAbsWideHeadBytes = kDNope * kAbsWideRowBytes;    // 16 KB: one he
 constexpr int kAbsWideBytes = kAbsWideHeads * kAbsWideHeadBytes;   // 64 KB
 constexpr int kAbsWideGroups = (kHeads / kAbsWideHeads) * (kDLat / kAbsWideCols);   // 256
 static_assert(2 * kAbsWideGroups == kAbsorbGroups, "a wide workgroup covers two narrow ones' flags");
+// one 32-row tile of the workgroup's results: 32 rows x 4 column groups of 16
+// x 2 halves of 8 columns x 4 heads, 16 bytes each
+constexpr int kStageGranules = 32 * 4 * 2 * kAbsWideHeads;      // 1024
+constexpr int kStageBytes = kStageGranules * 16;                // 16 KB, two of them
+static_assert(kStageGranules == 4 * kPrepThreads, "four granules per thread");
+
+// Staging granule of (row in tile rl, column group c16l, half sel, head h4):
+// the index runs in the order of q_abs's fragment layout (the 4 heads of the
+// workgroup are 4 consecutive 16-byte slots of one line), XOR-swizzled in its
+// low 4 bits by the row so that the 32 rows one staging write covers spread
+// over the LDS banks.
+__device__ __forceinline__ int stage_off(int g) { return 16 * (g ^ ((g >> 5) & 15)); }
 
 // LDS byte offset of 16-byte granule g (0..7) of row k of head h4's slice.
 // Rows are 128 bytes; where bit 1 of k is set the row's two 64-byte halves
@@ -38,10 +50,17 @@ __device__ __forceinline__ int wl_off_wide(int h4, int k, int g) {
 // 64), every query row. Its slice is read as whole 128-byte lines; the 4
 // heads' results fill half of each 128-byte line of q_abs (8 consecutive heads
 // x 8 values), and the workgroup with the other 4 heads runs on the same XCD,
-// so the halves meet in its L2.
+// so the halves meet in its L2. Each 32-row tile's results go through LDS
+// (two 16 KB buffers in the slice's space, free once every wavefront holds
+// its A fragments) so that the 4 heads leave as 64-byte runs, four
+// consecutive lanes' 16-byte stores: written straight from the accumulators
+// every 16-byte fragment slot was a separate piece of a different 128-byte
+// line, and at 256 query rows those scattered stores took over a third of
+// the launch (29 against 18 us without them).
 __device__ __forceinline__ void absorb_block_wide(const uint16_t* __restrict__ q_nope,
                                                   const uint16_t* __restrict__ w_uk, _Float16* __restrict__ q_abs,
-                                                  int rows, int g4, int cb, char* wl, int* __restrict__ range_flag) {
+                                                  int rows, int g4, int cb, char* wl,
+                                                  int* __restrict__ range_flag) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
@@ -100,11 +119,17 @@ __device__ __forceinline__ void absorb_block_wide(const uint16_t* __restrict__ q
       a[ct][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
-  const int hg = h >> 5, hj = h & 31;
+  // the slice's LDS becomes the staging space once every wavefront holds its
+  // A fragments (one workgroup then fits beside the plan's on a CU)
+  static_assert(2 * kStageBytes <= kAbsWideBytes, "staging fits the slice buffer");
+  char* const stage = wl;
+  __syncthreads();
+  const int hg = h >> 5;                  // the 4 heads share their 32-head group
+  const int hj0 = (kAbsWideHeads * g4) & 31;   // the first one's place in it
   bool out_of_range = false;   // a value past kQAbsMax (or not finite)
   // one 32-row tile; its buffer then loads the tile three further on
   auto tile = [&](int r0, u32x4 (&bt)[8]) {
-    const int r = r0 + (lane & 31);
+    const int rl = lane & 31, r = r0 + rl;
     f32x16 acc[2] = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -113,6 +138,9 @@ __device__ __forceinline__ void absorb_block_wide(const uint16_t* __restrict__ q
         acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct][ks], __builtin_bit_cast(bf16x8, bt[ks]), acc[ct], 0,
                                                           0, 0);
     if (r0 + 96 < rows) load_q(r0 + 96, bt);
+    // tiles alternate between the two staging buffers: the barrier below
+    // also orders this tile's writes after every read of the tile two back
+    char* stg = stage + ((r0 >> 5) & 1) * kStageBytes;
     if (r < rows) {
       // acc[ct][4 q + e] holds column 64 cb + 32 ct + 8 q + 4 half + e of row
       // r; stored scaled by kQScale (a power of two: the rounding to fp16 is
@@ -125,12 +153,28 @@ __device__ __forceinline__ void absorb_block_wide(const uint16_t* __restrict__ q
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c16 = 4 * cb + 2 * ct + (q >> 1);   // column / 16
+          // column group 2 ct + q / 2 of the tile's four, half q % 2 of it
+          const int g = rl * 32 + ((2 * ct + (q >> 1)) * 2 + (q & 1)) * kAbsWideHeads + w;
           f16x4 v = {(_Float16)(acc[ct][4 * q] * kQScale), (_Float16)(acc[ct][4 * q + 1] * kQScale),
                      (_Float16)(acc[ct][4 * q + 2] * kQScale), (_Float16)(acc[ct][4 * q + 3] * kQScale)};
-          const size_t frag = (((size_t)r * 4 + hg) * 32 + c16) * 64 + hj + 32 * (q & 1);
-          *(f16x4*)(q_abs + frag * 8 + 4 * half) = v;
+          *(f16x4*)(stg + stage_off(g) + 8 * half) = v;
         }
+    }
+    __syncthreads();
+    // granule G = 4 run + head: run (rl, c16l, sel) is 64 contiguous bytes of
+    // q_abs, fragment slots hj0 .. hj0 + 3 (+ 32 sel) of the 1 KB fragment
+    // block (row, hg, column group 4 cb + c16l)
+#pragma unroll
+    for (int n = 0; n < kStageGranules / kPrepThreads; ++n) {
+      const int G = t + kPrepThreads * n;
+      const int run = G >> 2, hq = G & 3;
+      const int rr = r0 + (run >> 3);
+      if (rr < rows) {
+        const u32x4 v = *(const u32x4*)(stg + stage_off(G));
+        const int c16 = 4 * cb + ((run >> 1) & 3);
+        const size_t frag = (((size_t)rr * 4 + hg) * 32 + c16) * 64 + hj0 + hq + 32 * (run & 1);
+        *(u32x4*)(q_abs + frag * 8) = v;
+      }
     }
   };
   for (int r0 = 0; r0 < rows; r0 += 96) {
@@ -148,7 +192,7 @@ __device__ __forceinline__ void absorb_block_wide(const uint16_t* __restrict__ q
 }
 
 // the same launch with the wide absorb tile (from kAbsWideRows query rows on)
-__global__ __launch_bounds__(kPrepThreads) void prep_wide_kernel(
+__global__ __launch_bounds__(kPrepThreads, 2) void prep_wide_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_table, int mbps, int num_blocks, int batch, int max_len, int split_target, int max_rounds, int positions,
     int depth, int max_chunks, WorkItem* __restrict__ work, SeqInfo* __restrict__ seqinfo,
     int* __restrict__ meta, const uint16_t* __restrict__ q_nope,
