@@ -147,3 +147,47 @@ def test_debug_build_refuses_a_shared_new_token_slot_in_the_append():
     assert st == PRE, st
     assert (cache.cpu().numpy() == 0x3f80).all(), "the append wrote rows after refusing its inputs"
     lib.mla_decode_destroy(ctx)
+
+
+def test_debug_build_checks_the_naive_path():
+    """mla_naive_run of the debug build: a prefill whose table repeats one of
+    the sequence's blocks is refused before any launch; the valid table gives
+    the release build's output bit for bit."""
+    import torch
+    from mla_latent_kv_amd import binding, device
+    lib = _dbg()
+    batch = synth.make_batch(synth.Spec("dbg_naive", 1, 200, (300,)), seed=73)
+    d = device.upload(batch)
+    dec = binding.MLADecoder(0, max_q_tokens=2)
+    w_uk, w_uv = dec.pack(d["w_uk"]), dec.pack(d["w_uv"])
+    ref = dec.naive(d["q_nope"], d["q_pe"], w_uk, w_uv, d["kv_cache"], d["block_table"], d["seq_lens"],
+                    d["max_seq_len"])
+    torch.cuda.synchronize()
+    ctx = _ctx(lib)
+    B, Sq = d["q_nope"].shape[:2]
+    n = ctypes.c_size_t()
+    assert lib.mla_naive_workspace_size(ctx, B, d["max_seq_len"], ctypes.byref(n)) == 0
+    ws = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+
+    def run(table, out):
+        args = binding.MlaNaiveArgs(
+            d["q_nope"].data_ptr(), d["q_pe"].data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+            d["kv_cache"].data_ptr(), table.data_ptr(), d["seq_lens"].data_ptr(), out.data_ptr(),
+            d["kv_cache"].shape[0], B, Sq, table.shape[1], d["max_seq_len"])
+        st = lib.mla_naive_run(ctx, ctypes.byref(args), ws.data_ptr(), n.value,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        return st
+
+    say("case debug build: naive prefill, block repeated within the sequence")
+    bad = d["block_table"].clone()
+    bad[0, 3] = bad[0, 1]              # blocks 1 and 3 of the 5 the sequence uses
+    out = torch.full_like(ref, 7.25)
+    assert run(bad, out) == PRE
+    assert (out.cpu().numpy() == 7.25).all(), "a kernel ran on refused inputs"
+    say("case debug build: naive prefill, valid")
+    out = torch.full_like(ref, float("nan"))
+    assert run(d["block_table"], out) == 0
+    assert np.array_equal(out.cpu().numpy(), ref.cpu().numpy())
+    lib.mla_decode_destroy(ctx)
+    dec.close()
