@@ -227,3 +227,32 @@ def test_large_batches(spec, n_sample=256):
     bs = rng.choice(spec.batch, n_sample, replace=False)
     sample = [(int(b), int(rng.integers(0, 128))) for b in bs]
     assert_parity(got, oracle(batch, sample=sample), f"{spec.name} {n_sample} sampled (b, h)")
+
+
+def _random_case(k):
+    """Seeded random batch k: batch size, query tokens, a length mix with
+    empty sequences, histories shorter than the query tokens and ragged long
+    ones, host bound slack, a split target and the query scale."""
+    rng = np.random.default_rng(1000 + k)
+    B = int(rng.integers(1, 49))
+    sq = int(rng.integers(1, 3))
+    kinds = rng.random(B)
+    lens = np.where(kinds < 0.15, 0,
+                    np.where(kinds < 0.25, rng.integers(1, sq + 1, B), rng.integers(1, 4001, B)))
+    if lens.max() == 0:
+        lens[0] = 1
+    slack = int(rng.choice([0, 1, 63, 200]))
+    spec = synth.Spec(f"random{k}", B, sq, tuple(int(x) for x in lens),
+                      q_scale=float(rng.choice([1.0, 3.0])), max_seq_len=int(lens.max()) + slack)
+    split = int(rng.choice([0, 1, 5, 13, 64, 300]))
+    return spec, split
+
+
+@pytest.mark.parametrize("k", range(10))
+def test_random_batches_every_output(k):
+    spec, split = _random_case(k)
+    batch = synth.make_batch(spec, seed=2000 + k)
+    say(f"case {spec.name}: B={spec.batch} Sq={spec.q_tokens} split={split} "
+        f"max_seq_len={batch['max_seq_len']} lens={batch['seq_lens'].tolist()}")
+    got = run_gpu(batch, split_target=split)
+    assert_parity(got, oracle(batch, path="absorb"), f"{spec.name} every output")
