@@ -37,6 +37,24 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, name), name
 
 
+def test_debug_build_exports_the_same_symbols():
+    """libmla_decode_debug.so (the ABI compiled with host-side precondition
+    checks) loads and exports every symbol the release library does."""
+    from mla_latent_kv_amd import binding
+    _lib()
+    if not os.path.exists(binding.DEBUG_LIB_PATH):
+        from mla_latent_kv_amd import build
+        build.build()
+    src = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(mla_\w+)\s*\(", src, re.M))
+    dbg = binding.load_library(binding.DEBUG_LIB_PATH)
+    for name in declared:
+        assert hasattr(dbg, name), name
+    # argument errors come back before any device call in both builds
+    assert dbg.mla_decode_run(None, None, None, 0, None) == -1
+    assert dbg.mla_decode_status_string(-6) == b"inputs break a documented precondition"
+
+
 def test_status_strings():
     from mla_latent_kv_amd import binding
     _lib()
