@@ -256,3 +256,26 @@ def test_random_batches_every_output(k):
         f"max_seq_len={batch['max_seq_len']} lens={batch['seq_lens'].tolist()}")
     got = run_gpu(batch, split_target=split)
     assert_parity(got, oracle(batch, path="absorb"), f"{spec.name} every output")
+
+
+def _far_cache_batch():
+    """One two-token sequence of 2^20 + 1000 cached tokens whose blocks sit
+    at ids 23000 and up of a 40000-block cache (2.95 GB, so block byte
+    offsets pass 2^31); every other block is bf16 NaN, so a read of any block
+    the table does not name would show in the output."""
+    batch = synth.make_batch(synth.Spec("far_1m", 1, 2, ((1 << 20) + 1000,)), seed=77)
+    nb = batch["cache"].shape[0]
+    far = np.full((40000,) + batch["cache"].shape[1:], synth.BF16_NAN, dtype=batch["cache"].dtype)
+    far[23000:23000 + nb] = batch["cache"]
+    batch["cache"] = far
+    batch["block_table"] = np.where(batch["block_table"] >= 0, batch["block_table"] + 23000, -1).astype(np.int32)
+    return batch
+
+
+def test_cache_past_2gib_and_a_million_token_history():
+    batch = _far_cache_batch()
+    say(f"case far_1m: L={int(batch['seq_lens'][0])} Sq=2, cache {batch['cache'].nbytes / 1e9:.2f} GB, "
+        f"blocks {int(batch['block_table'].min())}..{int(batch['block_table'].max())}")
+    got = run_gpu(batch)
+    assert np.isfinite(got).all()
+    assert_parity(got, oracle(batch, path="absorb"), "far_1m every output")
